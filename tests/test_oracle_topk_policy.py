@@ -1,0 +1,198 @@
+"""Pins of the oracle's block top-k, policy run and policy dynamic program
+(CPU only): library sorts, hand-derived fixtures, brute force, closed forms."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_layer_reuse_amd import synth, workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BLOCK = 128
+
+
+def test_topk_golden():
+    spec = json.load(open(os.path.join(GOLDEN, "topk_worked.json")))
+    for case in spec["cases"]:
+        s = np.array(case["scores"], np.float64)[None, None]
+        ctx = np.array([len(case["scores"]) * BLOCK], np.int32)
+        idx, _ = oracle.topk(s, ctx, case["k"])
+        assert idx[0, 0].tolist() == case["idx"], case
+
+
+def test_topk_matches_lexsort():
+    rng = np.random.default_rng(1)
+    for trial in range(50):
+        B, Hkv, maxb = 3, 2, int(rng.integers(1, 40))
+        # coarse values make exact ties frequent
+        score = rng.integers(0, 6, size=(B, Hkv, maxb)).astype(np.float64) / 7.0
+        ctx = rng.integers(0, maxb * BLOCK + 1, size=B).astype(np.int32)
+        k = int(rng.integers(1, maxb + 3))
+        idx, margin = oracle.topk(score, ctx, k)
+        for b in range(B):
+            N = (int(ctx[b]) + BLOCK - 1) // BLOCK
+            keff = min(k, N)
+            for g in range(Hkv):
+                order = np.lexsort((np.arange(N), -score[b, g, :N]))   # numpy sort
+                want = sorted(order[:keff].tolist()) + [-1] * (k - keff)
+                assert idx[b, g].tolist() == want
+                if keff < N:
+                    kth = score[b, g, order[keff - 1]]
+                    nxt = score[b, g, order[keff]]
+                    want_m = (kth - nxt) / kth if kth > 0 else 0.0
+                    assert margin[b, g] == pytest.approx(want_m)
+                else:
+                    assert np.isinf(margin[b, g])
+
+
+def test_topk_special_cases():
+    s = np.full((1, 1, 10), 0.25)
+    idx, m = oracle.topk(s, np.array([10 * BLOCK], np.int32), 4)
+    assert idx[0, 0].tolist() == [0, 1, 2, 3] and m[0, 0] == 0.0
+    idx, _ = oracle.topk(s, np.array([10 * BLOCK], np.int32), 12)
+    assert idx[0, 0].tolist() == list(range(10)) + [-1, -1]
+    idx, _ = oracle.topk(s, np.array([0], np.int32), 3)
+    assert idx[0, 0].tolist() == [-1, -1, -1]
+
+
+def _tiny_layers(ctx=(1024,), L=4, seed=100, dtype="f32"):
+    layers = []
+    for l in range(L):
+        lay = synth.make_layer(batch=len(ctx), num_q_heads=4, num_kv_heads=2, head_dim=32,
+                               dtype=dtype, ctx_lens=ctx, seed=seed + 16 * l)
+        layers.append(synth.layer_to_oracle(lay))
+    return layers
+
+
+def test_run_policy_all_reset_equals_full():
+    layers = _tiny_layers(ctx=(1000, 300))
+    res = oracle.run_policy(layers, [0, 1, 2, 3], 2, num_kv_heads=2)
+    for lay, r in zip(layers, res):
+        out, lse, _ = oracle.attend(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"],
+                                    lay["ctx"], num_kv_heads=2)
+        np.testing.assert_array_equal(r["out"], out)
+        np.testing.assert_array_equal(r["lse"], lse)
+
+
+def test_run_policy_k_covering_all_blocks_equals_full():
+    layers = _tiny_layers(ctx=(1000, 300))
+    res = oracle.run_policy(layers, [0, 0, 0, 3], 8, num_kv_heads=2)
+    for lay, r in zip(layers, res):
+        out, lse, _ = oracle.attend(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"],
+                                    lay["ctx"], num_kv_heads=2)
+        np.testing.assert_allclose(r["out"], out, atol=1e-12)
+        np.testing.assert_allclose(r["lse"], lse, atol=1e-12)
+
+
+def test_run_policy_reuse_uses_source_indices():
+    layers = _tiny_layers(ctx=(1024,))
+    res = oracle.run_policy(layers, [0, 0, 2, 2], 2, num_kv_heads=2)
+    assert np.array_equal(res[1]["idx"], res[0]["idx"])
+    assert np.array_equal(res[3]["idx"], res[2]["idx"])
+    lay = layers[1]
+    out, lse, _ = oracle.attend(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
+                                num_kv_heads=2, sel=res[0]["idx"], k=2)
+    np.testing.assert_array_equal(res[1]["out"], out)
+
+
+def test_run_policy_rejects_malformed():
+    layers = _tiny_layers(L=3)
+    for bad in ([1, 1, 2], [0, 2, 2], [0, 1, 0], [0, 0, 1]):
+        with pytest.raises(ValueError):
+            oracle.run_policy(layers, bad, 2, num_kv_heads=2)
+
+
+# ---------------------------------------------------------------- policy DP
+def _golden_policy():
+    spec = json.load(open(os.path.join(GOLDEN, "policy_worked.json")))
+    L = spec["L"]
+    M = np.zeros((L, L), np.float32)
+    for key, val in spec["M_lower"].items():
+        j, i = map(int, key.split(","))
+        M[j, i] = np.float32(val)
+    return spec, M
+
+
+def test_policy_golden():
+    spec, M = _golden_policy()
+    L = spec["L"]
+    for case in spec["cases"]:
+        force = [j in case["force"] for j in range(L)]
+        theta = float(np.float32(case["theta"]))
+        for fn in (oracle.policy_dp, oracle.brute_force_policy):
+            src, r, s = fn(M, theta, force)
+            assert src == case["src"], (fn.__name__, case)
+            assert r == case["resets"]
+            want = float(np.float64(np.float32(0.9)) + np.float64(np.float32(0.95))) \
+                if case["sim"] == "1.85" else None
+            if want is not None:
+                assert abs(s - want) < 1e-12
+            else:
+                assert abs(s - float(case["sim"])) < 1e-6
+
+
+@pytest.mark.parametrize("decay", [3.0, 6.0, 10.0])
+def test_policy_dp_matches_bruteforce(decay):
+    rng = np.random.default_rng(int(decay * 10))
+    for trial in range(70):
+        L = int(rng.integers(1, 13))
+        M = synth.similarity_matrix(L, decay, noise=0.03, seed=int(rng.integers(1 << 30)))
+        theta = float(np.float32(rng.choice([0.5, 0.6, 0.7, 0.8, 0.9, 0.95])))
+        force = (rng.random(L) < 0.2).tolist()
+        got = oracle.policy_dp(M, theta, force)
+        want = oracle.brute_force_policy(M, theta, force)
+        assert got[0] == want[0], (L, theta, force)
+        assert got[1] == want[1]
+        assert abs(got[2] - want[2]) < 1e-12
+        assert oracle.policy_cost(M, theta, got[0], force) is not None
+
+
+def test_policy_dp_ties_match_bruteforce():
+    # quantised similarities make many exactly tied optima
+    rng = np.random.default_rng(9)
+    for trial in range(150):
+        L = int(rng.integers(2, 11))
+        M = np.tril(rng.integers(0, 5, size=(L, L)) / 4.0).astype(np.float32)
+        theta = float(rng.choice([0.2, 0.5, 0.7]))
+        force = (rng.random(L) < 0.15).tolist()
+        assert oracle.policy_dp(M, theta, force)[0] == \
+            oracle.brute_force_policy(M, theta, force)[0]
+
+
+def test_policy_closed_forms():
+    L = 30
+    for w in (1, 2, 3, 5, 7):
+        # banded similarity: 1 within distance < w, else 0
+        M = np.zeros((L, L), np.float32)
+        for j in range(L):
+            for i in range(j + 1):
+                M[j, i] = 1.0 if j - i < w else 0.0
+        src, r, s = oracle.policy_dp(M, 0.5)
+        assert r == -(-L // w)
+        assert [j for j in range(L) if src[j] == j] == list(range(0, L, w))
+        assert s == L - r
+    M = synth.similarity_matrix(L, 6.0, seed=1)
+    src, r, _ = oracle.policy_dp(M, 1.0)
+    assert src == list(range(L)) and r == L
+    force = [j in (0, 5, 17) for j in range(L)]
+    src, r, _ = oracle.policy_dp(M, -0.5, force)
+    assert [j for j in range(L) if src[j] == j] == [0, 5, 17] and r == 3
+
+
+def test_policy_dp_workload_sizes():
+    # the two DP workloads: large L, results feasible and no worse than the
+    # natural greedy policy (reuse while allowed)
+    for wl in (W.LLAMA3_8B_B8_64K_DP, W.LLAMA3_70B_128K_DP):
+        M = synth.workload_similarity(wl)
+        for theta in wl.dp_theta:
+            force = [j in wl.dp_force for j in range(wl.layers)]
+            src, r, s = oracle.policy_dp(M, theta, force)
+            assert oracle.policy_cost(M, theta, src, force) == (r, pytest.approx(s))
+            greedy = [0]
+            for j in range(1, wl.layers):
+                i = greedy[-1]
+                greedy.append(i if (not force[j] and M[j, i] > theta) else j)
+            gr = oracle.policy_cost(M, theta, greedy, force)
+            assert r <= gr[0]
