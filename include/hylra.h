@@ -1,0 +1,152 @@
+/*
+ * hylra.h -- C ABI of the MI355X (gfx950) HyLRA decode-phase hybrid attention.
+ *
+ * Method: "HyLRA: Hybrid Layer Reuse Attention for Efficient Long-Context
+ * Inference" (technical summary).  Sensitive ("reset") layers run standard
+ * full attention and extract the top-k indices, which are passed forward
+ * (section 2.3, Sensitive Layers); tolerant ("reuse") layers attend only to
+ * the KV subset named by the carried indices (section 2.3, Tolerant Layers);
+ * selection works on fixed 128-token blocks (section 2.4, Block-level
+ * Sparsity); the per-layer reset/reuse policy comes from an offline dynamic
+ * program over a lower-triangular similarity matrix M with a fidelity
+ * threshold theta (section 2.2).
+ *
+ * Conventions shared by every entry point
+ *   - All device pointers are HIP device memory owned by the caller.  The
+ *     library never allocates, frees, copies device-to-host or synchronises;
+ *     device work is enqueued on `hip_stream` (a hipStream_t, NULL = the
+ *     default stream) and is asynchronous.
+ *   - Element type of q / K / V: HYLRA_F32 (IEEE float32) or HYLRA_BF16
+ *     (bfloat16).  Outputs and scores are float32.
+ *   - Layouts (row-major, innermost last):
+ *       q            [B][Hq][d]
+ *       K pool       [num_pages][Hkv][128][d]   token-major page tile
+ *       V pool       [num_pages][Hkv][d][128]   dimension-major page tile
+ *       block_table  [B][max_blocks_per_seq] int32, logical block -> page
+ *       ctx_lens     [B] int32, tokens of each sequence (device memory)
+ *       out          [B][Hq][d] float32, lse [B][Hq] float32 (natural log)
+ *       block_score  [B][Hkv][max_blocks_per_seq] float32
+ *       idx          [B][Hkv][k] int32, ascending block ids, -1 padded
+ *     Query head h uses KV head h / (Hq / Hkv).  Pointers must be 16-byte
+ *     aligned.  Every page named by the table holds 128 tokens of storage.
+ *   - ctx_lens values are clamped to [0, 128 * max_blocks_per_seq].  A
+ *     sequence with no tokens gets out = 0, lse = -inf, idx = -1.
+ *   - A block-table entry outside [0, num_pages) makes that block empty
+ *     (never read); a selected block id outside [0, ceil(T/128)) is skipped.
+ *   - Return values: HYLRA_OK or an error code; argument checks run on the
+ *     host before anything is enqueued, and a failed check enqueues nothing.
+ *     hylra_last_error() gives a thread-local message for the last failure.
+ */
+#ifndef HYLRA_H
+#define HYLRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hylra_status;
+#define HYLRA_OK 0
+#define HYLRA_E_INVALID_ARG 1 /* null pointer, bad size, inconsistent shape */
+#define HYLRA_E_UNSUPPORTED 2 /* valid but not implemented (head_dim, group size, ...) */
+#define HYLRA_E_BAD_POLICY 3  /* malformed per-layer source list */
+#define HYLRA_E_WORKSPACE 4   /* workspace missing or smaller than required */
+#define HYLRA_E_DEVICE 5      /* HIP launch / runtime error (message in hylra_last_error) */
+
+#define HYLRA_F32 0
+#define HYLRA_BF16 1
+#define HYLRA_BLOCK_TOKENS 128
+
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;           /* d: 64 or 128 */
+  int32_t block_size;         /* must be 128 (section 2.4 block granularity) */
+  int32_t dtype;              /* HYLRA_F32 or HYLRA_BF16 */
+  int32_t max_blocks_per_seq; /* block_table row stride, 1 .. 8192 */
+  float scale;                /* logit scale; 0 selects 1/sqrt(head_dim) */
+} hylra_shape;
+
+typedef struct {
+  const void *k_pool;         /* [num_pages][Hkv][128][d] */
+  const void *v_pool;         /* [num_pages][Hkv][d][128] */
+  int64_t num_pages;          /* >= 1 */
+  const int32_t *block_table; /* [B][max_blocks_per_seq] */
+  const int32_t *ctx_lens;    /* [B] */
+} hylra_kv;
+
+/* Bytes of device workspace that every entry point below needs for `shape`
+ * and top-k `k` (k <= 0 allowed when no sparse/top-k call is made).  The
+ * caller allocates it once and may reuse it across calls on one stream. */
+hylra_status hylra_workspace_size(const hylra_shape *shape, int32_t k, size_t *bytes);
+
+/* Full decode attention of one layer (section 2.3, sensitive layers):
+ *   s_t = scale * q_h . K_t, p = softmax over all t < T_b,
+ *   out_h = sum_t p_t V_t, lse_h = ln sum_t exp(s_t),
+ * and, when block_score is non-NULL, the block score of every 128-token
+ * block n < ceil(T_b/128) of KV head g:
+ *   score[b][g][n] = sum over query heads h of group g of sum_{t in n} p_t,
+ * entries n >= ceil(T_b/128) set to 0.  lse may be NULL. */
+hylra_status hylra_decode_full(const hylra_shape *shape, const void *q, const hylra_kv *kv,
+                               float *out, float *lse, float *block_score, void *workspace,
+                               size_t workspace_bytes, void *hip_stream);
+
+/* Top-k blocks of a score array (section 2.3: the top-k indices extracted at
+ * sensitive layers).  Per (b, g): the k_eff = min(k, ceil(T_b/128)) blocks
+ * with the largest score, ties going to the lower block id, written in
+ * ascending id order to idx[b][g][0..k_eff) and -1 after.  Scores must be
+ * finite and >= 0.  k >= 1. */
+hylra_status hylra_block_topk(const hylra_shape *shape, const float *block_score,
+                              const int32_t *ctx_lens, int32_t k, int32_t *idx,
+                              void *hip_stream);
+
+/* Decode attention restricted to the selected blocks (section 2.3, tolerant
+ * layers): U = tokens t < T_b whose block id is in idx[b][g][0..k) (negative
+ * entries are padding); softmax and output over U only.  An empty U gives
+ * out = 0 and lse = -inf.  lse may be NULL. */
+hylra_status hylra_decode_sparse(const hylra_shape *shape, const void *q, const hylra_kv *kv,
+                                 const int32_t *idx, int32_t k, float *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* One decode step of the hybrid policy over num_layers layers (section 2.3):
+ * layer j with src[j] == j resets (full attention, block scores, top-k, the
+ * result becomes the carried index set); a layer with src[j] == src[j-1]
+ * reuses the carried set (sparse attention).  src is a host array and must
+ * satisfy src[0] == 0 and src[j] in {j, src[j-1]} (HYLRA_E_BAD_POLICY
+ * otherwise).  q, kv, out and lse are host arrays of num_layers entries (lse
+ * may be NULL, or hold NULL entries).  idx_log (device, nullable)
+ * [num_layers][B][Hkv][k] receives the index set each layer computed or
+ * reused.  Everything is enqueued on one stream with no host synchronisation. */
+hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, const int32_t *src,
+                              int32_t k, const void *const *q, const hylra_kv *kv,
+                              float *const *out, float *const *lse, int32_t *idx_log,
+                              void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Offline policy dynamic program (section 2.2), host only, synchronous.
+ * M: host [L][L] float32, row = target layer, column = source layer
+ * (M[j*L + i] = similarity of reusing layer i's indices at layer j, i <= j;
+ * the upper triangle and the diagonal are not read).  A reuse move of layer
+ * j from source i is allowed when force_reset[j] == 0 and M[j][i] > theta.
+ * Objective: fewest resets, then the largest summed similarity of the reuse
+ * moves; among optima (equal resets, sums within 1e-12) the policy that
+ * reuses at the earliest layer where they differ.  Layer 0 always resets.
+ * Writes src_out[L]; num_resets and sim_sum may be NULL.  1 <= L <= 1024;
+ * M entries and theta must not be NaN. */
+hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
+                             const uint8_t *force_reset, int32_t *src_out, int32_t *num_resets,
+                             double *sim_sum);
+
+/* Static string for a status code. */
+const char *hylra_status_str(hylra_status status);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *hylra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYLRA_H */

@@ -1,0 +1,432 @@
+// C ABI of libhylra: argument validation, workspace layout, launch sequencing
+// of the decode attention kernels, and the host-side policy dynamic program.
+//
+// Method: "HyLRA: Hybrid Layer Reuse Attention for Efficient Long-Context
+// Inference", technical summary 2.2 (offline policy DP) and 2.3 (hybrid
+// execution of the policy during decoding).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/hylra.h"
+#include "hylra_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hylra_status fail(hylra_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hylra_status ok() {
+  g_last_error.clear();
+  return HYLRA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+hylra_status check_shape(const hylra_shape *s) {
+  if (s == nullptr) return fail(HYLRA_E_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1) return fail(HYLRA_E_INVALID_ARG, "batch must be >= 1 (got %d)", s->batch);
+  if (s->num_kv_heads < 1 || s->num_q_heads < s->num_kv_heads ||
+      s->num_q_heads % s->num_kv_heads != 0)
+    return fail(HYLRA_E_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads / s->num_kv_heads > hylra::kMaxGroup)
+    return fail(HYLRA_E_UNSUPPORTED, "group size %d exceeds %d query heads per KV head",
+                s->num_q_heads / s->num_kv_heads, hylra::kMaxGroup);
+  if (s->num_kv_heads > 65535 || s->batch > 65535)
+    return fail(HYLRA_E_UNSUPPORTED, "batch and num_kv_heads must be <= 65535");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(HYLRA_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", s->head_dim);
+  if (s->block_size != HYLRA_BLOCK_TOKENS)
+    return fail(HYLRA_E_UNSUPPORTED, "block_size must be 128 (got %d)", s->block_size);
+  if (s->dtype != HYLRA_F32 && s->dtype != HYLRA_BF16)
+    return fail(HYLRA_E_INVALID_ARG, "dtype must be HYLRA_F32 or HYLRA_BF16 (got %d)", s->dtype);
+  if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > hylra::kMaxBlocks)
+    return fail(HYLRA_E_UNSUPPORTED, "max_blocks_per_seq must be in [1, %d] (got %d)",
+                hylra::kMaxBlocks, s->max_blocks_per_seq);
+  if (!(s->scale >= 0.f) || isinf(s->scale))
+    return fail(HYLRA_E_INVALID_ARG, "scale must be finite and >= 0");
+  return HYLRA_OK;
+}
+
+hylra_status check_kv(const hylra_kv *kv) {
+  if (kv == nullptr) return fail(HYLRA_E_INVALID_ARG, "kv is NULL");
+  if (kv->k_pool == nullptr || kv->v_pool == nullptr || kv->block_table == nullptr ||
+      kv->ctx_lens == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "kv has a NULL pointer");
+  if (!aligned16(kv->k_pool) || !aligned16(kv->v_pool))
+    return fail(HYLRA_E_INVALID_ARG, "K/V pools must be 16-byte aligned");
+  if (kv->num_pages < 1) return fail(HYLRA_E_INVALID_ARG, "num_pages must be >= 1");
+  return HYLRA_OK;
+}
+
+float logit_scale_log2(const hylra_shape *s) {
+  const float scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+  return scale * 1.4426950408889634f;
+}
+
+// Workspace carve-up shared by every entry point.
+struct Workspace {
+  float *part_ml;
+  float *part_o;
+  float *stats;
+  float *head_mass;
+  int32_t *idx;
+  size_t bytes;
+};
+
+int max_nsplit(const hylra_shape *s, int k) {
+  const hylra::SplitPlan f = hylra::plan_full(s->batch, s->num_kv_heads, s->max_blocks_per_seq);
+  int n = f.nsplit;
+  if (k > 0) {
+    const hylra::SplitPlan p =
+        hylra::plan_sparse(s->batch, s->num_kv_heads, s->max_blocks_per_seq, k);
+    if (p.nsplit > n) n = p.nsplit;
+  }
+  return n;
+}
+
+Workspace layout(const hylra_shape *s, int k, void *base) {
+  const size_t B = s->batch, Hq = s->num_q_heads, Hkv = s->num_kv_heads, D = s->head_dim;
+  const size_t mb = s->max_blocks_per_seq;
+  const size_t ns = max_nsplit(s, k);
+  const size_t a = 256;
+  size_t off = 0;
+  Workspace w{};
+  char *p = static_cast<char *>(base);
+  auto take = [&](size_t bytes) -> char * {
+    char *r = p ? p + off : nullptr;
+    off = round_up(off + bytes, a);
+    return r;
+  };
+  w.part_ml = reinterpret_cast<float *>(take(B * Hq * ns * 2 * sizeof(float)));
+  w.part_o = reinterpret_cast<float *>(take(B * Hq * ns * D * sizeof(float)));
+  w.stats = reinterpret_cast<float *>(take(B * Hq * mb * hylra::kChunksPerBlock * 2 * sizeof(float)));
+  w.head_mass = reinterpret_cast<float *>(take(B * Hq * mb * sizeof(float)));
+  w.idx = reinterpret_cast<int32_t *>(take(B * Hkv * (size_t)(k > 0 ? k : 1) * sizeof(int32_t)));
+  w.bytes = off;
+  return w;
+}
+
+hylra_status check_ws(const hylra_shape *s, int k, void *ws, size_t ws_bytes, Workspace &w) {
+  w = layout(s, k, ws);
+  if (ws == nullptr || ws_bytes < w.bytes)
+    return fail(HYLRA_E_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", w.bytes, ws_bytes,
+                ws == nullptr ? ", NULL" : "");
+  if (!aligned16(ws)) return fail(HYLRA_E_INVALID_ARG, "workspace must be 16-byte aligned");
+  return HYLRA_OK;
+}
+
+hylra_status device_status(int code, const char *what) {
+  if (code == 0) return HYLRA_OK;
+  return fail(HYLRA_E_DEVICE, "%s: %s", what, hylra::device_error_string(code));
+}
+
+hylra::AttnArgs attn_args(const hylra_shape *s, const void *q, const hylra_kv *kv,
+                          const int32_t *sel, int k, const hylra::SplitPlan &plan,
+                          const Workspace &w, bool with_stats) {
+  hylra::AttnArgs a{};
+  a.q = q;
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.num_pages = kv->num_pages;
+  a.table = kv->block_table;
+  a.ctx = kv->ctx_lens;
+  a.sel = sel;
+  a.k = k;
+  a.max_blocks = s->max_blocks_per_seq;
+  a.num_q_heads = s->num_q_heads;
+  a.num_kv_heads = s->num_kv_heads;
+  a.group = s->num_q_heads / s->num_kv_heads;
+  a.scale_log2 = logit_scale_log2(s);
+  a.chunks_per_wg = plan.chunks_per_wg;
+  a.nsplit = plan.nsplit;
+  a.part_ml = w.part_ml;
+  a.part_o = w.part_o;
+  a.stats = with_stats ? w.stats : nullptr;
+  return a;
+}
+
+hylra::MergeArgs merge_args(const hylra::AttnArgs &a, const hylra_shape *s, float *out,
+                            float *lse, float *head_mass, int32_t *sel_log) {
+  hylra::MergeArgs m{};
+  m.part_ml = a.part_ml;
+  m.part_o = a.part_o;
+  m.stats = a.stats;
+  m.ctx = a.ctx;
+  m.sel = a.sel;
+  m.sel_log = sel_log;
+  m.k = a.k;
+  m.max_blocks = a.max_blocks;
+  m.num_q_heads = a.num_q_heads;
+  m.num_kv_heads = a.num_kv_heads;
+  m.group = a.group;
+  m.head_dim = s->head_dim;
+  m.chunks_per_wg = a.chunks_per_wg;
+  m.nsplit = a.nsplit;
+  m.out = out;
+  m.lse = lse;
+  m.head_mass = head_mass;
+  return m;
+}
+
+// Reset layer: full attention -> merge (out, lse, per-head block mass) ->
+// block score and/or top-k.
+hylra_status run_full(const hylra_shape *s, const void *q, const hylra_kv *kv, float *out,
+                      float *lse, float *block_score, int32_t *idx, int k, const Workspace &w,
+                      void *stream) {
+  const hylra::SplitPlan plan = hylra::plan_full(s->batch, s->num_kv_heads, s->max_blocks_per_seq);
+  const bool scores = block_score != nullptr || idx != nullptr;
+  hylra::AttnArgs a = attn_args(s, q, kv, nullptr, 0, plan, w, scores);
+  hylra_status st = device_status(hylra::launch_attn(a, s->dtype, s->head_dim, s->batch, stream),
+                                  "attention launch");
+  if (st) return st;
+  hylra::MergeArgs m = merge_args(a, s, out, lse, scores ? w.head_mass : nullptr, nullptr);
+  st = device_status(hylra::launch_merge(m, s->batch, stream), "merge launch");
+  if (st || !scores) return st;
+  hylra::TopkArgs t{};
+  t.mass = w.head_mass;
+  t.heads_per_row = s->num_q_heads / s->num_kv_heads;
+  t.ctx = kv->ctx_lens;
+  t.max_blocks = s->max_blocks_per_seq;
+  t.num_kv_heads = s->num_kv_heads;
+  t.score_out = block_score;
+  t.idx = idx;
+  t.k = k;
+  return device_status(hylra::launch_topk(t, s->batch, stream), "top-k launch");
+}
+
+// Reuse layer: attention over the selected blocks -> merge.
+hylra_status run_sparse(const hylra_shape *s, const void *q, const hylra_kv *kv,
+                        const int32_t *idx, int k, float *out, float *lse, int32_t *log,
+                        const Workspace &w, void *stream) {
+  const hylra::SplitPlan plan =
+      hylra::plan_sparse(s->batch, s->num_kv_heads, s->max_blocks_per_seq, k);
+  hylra::AttnArgs a = attn_args(s, q, kv, idx, k, plan, w, false);
+  hylra_status st = device_status(hylra::launch_attn(a, s->dtype, s->head_dim, s->batch, stream),
+                                  "attention launch");
+  if (st) return st;
+  hylra::MergeArgs m = merge_args(a, s, out, lse, nullptr, log);
+  return device_status(hylra::launch_merge(m, s->batch, stream), "merge launch");
+}
+
+}  // namespace
+
+namespace hylra {
+
+// Split plans: aim for about 1024 workgroups per launch (four per compute
+// unit on a 256-CU part) so the grid fills the chip at batch 1.
+constexpr long kTargetWorkgroups = 1024;
+
+SplitPlan plan_full(int batch, int num_kv_heads, int max_blocks) {
+  const long C = (long)kChunksPerBlock * max_blocks;
+  const long total = (long)batch * num_kv_heads * C;
+  long cpw = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  cpw = (cpw + 3) / 4 * 4;
+  if (cpw < 4) cpw = 4;
+  SplitPlan p;
+  p.chunks_per_wg = (int)cpw;
+  p.nsplit = (int)((C + cpw - 1) / cpw);
+  return p;
+}
+
+SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k) {
+  const long keff = k < max_blocks ? k : max_blocks;
+  const long C = (long)kChunksPerBlock * (keff > 0 ? keff : 1);
+  const long total = (long)batch * num_kv_heads * C;
+  long cpw = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  if (cpw > 4) cpw = (cpw + 3) / 4 * 4;
+  if (cpw < 1) cpw = 1;
+  SplitPlan p;
+  p.chunks_per_wg = (int)cpw;
+  p.nsplit = (int)((C + cpw - 1) / cpw);
+  return p;
+}
+
+}  // namespace hylra
+
+extern "C" {
+
+hylra_status hylra_workspace_size(const hylra_shape *shape, int32_t k, size_t *bytes) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (bytes == nullptr) return fail(HYLRA_E_INVALID_ARG, "bytes is NULL");
+  *bytes = layout(shape, k, nullptr).bytes;
+  return ok();
+}
+
+hylra_status hylra_decode_full(const hylra_shape *shape, const void *q, const hylra_kv *kv,
+                               float *out, float *lse, float *block_score, void *workspace,
+                               size_t workspace_bytes, void *hip_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (hylra_status st = check_kv(kv)) return st;
+  if (q == nullptr || out == nullptr) return fail(HYLRA_E_INVALID_ARG, "q and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(HYLRA_E_INVALID_ARG, "q and out must be 16-byte aligned");
+  Workspace w;
+  if (hylra_status st = check_ws(shape, 0, workspace, workspace_bytes, w)) return st;
+  if (hylra_status st = run_full(shape, q, kv, out, lse, block_score, nullptr, 0, w, hip_stream))
+    return st;
+  return ok();
+}
+
+hylra_status hylra_block_topk(const hylra_shape *shape, const float *block_score,
+                              const int32_t *ctx_lens, int32_t k, int32_t *idx, void *hip_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (block_score == nullptr || ctx_lens == nullptr || idx == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "block_score, ctx_lens and idx must be non-NULL");
+  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  hylra::TopkArgs t{};
+  t.mass = block_score;
+  t.heads_per_row = 1;
+  t.ctx = ctx_lens;
+  t.max_blocks = shape->max_blocks_per_seq;
+  t.num_kv_heads = shape->num_kv_heads;
+  t.score_out = nullptr;
+  t.idx = idx;
+  t.k = k;
+  if (hylra_status st = device_status(hylra::launch_topk(t, shape->batch, hip_stream), "top-k launch"))
+    return st;
+  return ok();
+}
+
+hylra_status hylra_decode_sparse(const hylra_shape *shape, const void *q, const hylra_kv *kv,
+                                 const int32_t *idx, int32_t k, float *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (hylra_status st = check_kv(kv)) return st;
+  if (q == nullptr || out == nullptr || idx == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "q, idx and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(HYLRA_E_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  Workspace w;
+  if (hylra_status st = check_ws(shape, k, workspace, workspace_bytes, w)) return st;
+  if (hylra_status st = run_sparse(shape, q, kv, idx, k, out, lse, nullptr, w, hip_stream))
+    return st;
+  return ok();
+}
+
+hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, const int32_t *src,
+                              int32_t k, const void *const *q, const hylra_kv *kv,
+                              float *const *out, float *const *lse, int32_t *idx_log,
+                              void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (num_layers < 1) return fail(HYLRA_E_INVALID_ARG, "num_layers must be >= 1");
+  if (src == nullptr || q == nullptr || kv == nullptr || out == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "src, q, kv and out must be non-NULL");
+  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (src[0] != 0) return fail(HYLRA_E_BAD_POLICY, "layer 0 must reset (src[0] = %d)", src[0]);
+  for (int j = 1; j < num_layers; ++j)
+    if (src[j] != j && src[j] != src[j - 1])
+      return fail(HYLRA_E_BAD_POLICY, "src[%d] = %d is neither %d nor src[%d] = %d", j, src[j], j,
+                  j - 1, src[j - 1]);
+  for (int j = 0; j < num_layers; ++j) {
+    if (hylra_status st = check_kv(&kv[j])) return fail(st, "layer %d: %s", j, hylra_last_error());
+    if (q[j] == nullptr || out[j] == nullptr || !aligned16(q[j]) || !aligned16(out[j]))
+      return fail(HYLRA_E_INVALID_ARG, "layer %d: q and out must be non-NULL and 16-byte aligned", j);
+  }
+  Workspace w;
+  if (hylra_status st = check_ws(shape, k, workspace, workspace_bytes, w)) return st;
+  const size_t row = (size_t)shape->batch * shape->num_kv_heads * k;
+  for (int j = 0; j < num_layers; ++j) {
+    float *lj = lse ? lse[j] : nullptr;
+    hylra_status st;
+    if (src[j] == j) {
+      int32_t *dst = idx_log ? idx_log + (size_t)j * row : w.idx;
+      st = run_full(shape, q[j], &kv[j], out[j], lj, nullptr, dst, k, w, hip_stream);
+    } else {
+      const int32_t *carried = idx_log ? idx_log + (size_t)src[j] * row : w.idx;
+      int32_t *log = idx_log ? idx_log + (size_t)j * row : nullptr;
+      st = run_sparse(shape, q[j], &kv[j], carried, k, out[j], lj, log, w, hip_stream);
+    }
+    if (st) return fail(st, "layer %d: %s", j, hylra_last_error());
+  }
+  return ok();
+}
+
+hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
+                             const uint8_t *force_reset, int32_t *src_out, int32_t *num_resets,
+                             double *sim_sum) {
+  const int L = num_layers;
+  if (L < 1 || L > 1024) return fail(HYLRA_E_INVALID_ARG, "num_layers must be in [1, 1024] (got %d)", L);
+  if (M == nullptr || src_out == nullptr) return fail(HYLRA_E_INVALID_ARG, "M and src_out must be non-NULL");
+  if (isnan(theta)) return fail(HYLRA_E_INVALID_ARG, "theta is NaN");
+  for (int j = 0; j < L; ++j)
+    for (int i = 0; i < j; ++i)
+      if (isnan(M[(size_t)j * L + i])) return fail(HYLRA_E_INVALID_ARG, "M[%d][%d] is NaN", j, i);
+
+  auto reusable = [&](int i, int j) {  // layer j may reuse the indices of reset layer i
+    return !(force_reset && force_reset[j]) && (double)M[(size_t)j * L + i] > (double)theta;
+  };
+  // best (resets, similarity) of layers j+1 .. L-1 from state (i, j), i <= j
+  std::vector<int> br((size_t)L * L, 0);
+  std::vector<double> bs((size_t)L * L, 0.0);
+  auto at = [L](int i, int j) { return (size_t)i * L + j; };
+  for (int j = L - 2; j >= 0; --j) {
+    for (int i = 0; i <= j; ++i) {
+      int r = br[at(j + 1, j + 1)] + 1;
+      double s = bs[at(j + 1, j + 1)];
+      if (reusable(i, j + 1)) {
+        const int r2 = br[at(i, j + 1)];
+        const double s2 = bs[at(i, j + 1)] + (double)M[(size_t)(j + 1) * L + i];
+        if (r2 < r || (r2 == r && s2 > s)) {
+          r = r2;
+          s = s2;
+        }
+      }
+      br[at(i, j)] = r;
+      bs[at(i, j)] = s;
+    }
+  }
+  const int r_opt = 1 + br[at(0, 0)];
+  const double s_opt = bs[at(0, 0)];
+  // forward pass: reuse whenever a reuse continuation is still optimal
+  int i = 0, acc_r = 1;
+  double acc_s = 0.0;
+  src_out[0] = 0;
+  for (int j = 0; j + 1 < L; ++j) {
+    bool reuse = false;
+    if (reusable(i, j + 1)) {
+      const double gain = (double)M[(size_t)(j + 1) * L + i];
+      reuse = acc_r + br[at(i, j + 1)] == r_opt && acc_s + gain + bs[at(i, j + 1)] >= s_opt - 1e-12;
+      if (reuse) acc_s += gain;
+    }
+    if (!reuse) {
+      ++acc_r;
+      i = j + 1;
+    }
+    src_out[j + 1] = i;
+  }
+  if (num_resets) *num_resets = acc_r;
+  if (sim_sum) *sim_sum = acc_s;
+  return ok();
+}
+
+const char *hylra_status_str(hylra_status status) {
+  switch (status) {
+    case HYLRA_OK: return "ok";
+    case HYLRA_E_INVALID_ARG: return "invalid argument";
+    case HYLRA_E_UNSUPPORTED: return "unsupported";
+    case HYLRA_E_BAD_POLICY: return "malformed policy";
+    case HYLRA_E_WORKSPACE: return "workspace too small";
+    case HYLRA_E_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char *hylra_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+"""ctypes binding of libhylra.so (include/hylra.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI.  Tensors are torch tensors on the GPU (PyTorch
+provides device memory and streams); the binding checks dtypes, shapes and
+contiguity, fills the C descriptors and passes raw pointers plus the current
+HIP stream.  Importing this module loads the library and raises if it has not
+been built -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhylra.so")
+
+OK, E_INVALID_ARG, E_UNSUPPORTED, E_BAD_POLICY, E_WORKSPACE, E_DEVICE = range(6)
+F32, BF16 = 0, 1
+BLOCK = 128
+
+
+class HylraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("hylra status %d (%s): %s" % (status, _status_str(status), message))
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+                ("ctx_lens", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libhylra.so is not built (%s); run __graft_entry__.build() or "
+                          "python sparse_layer_reuse_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    SP, KP = ctypes.POINTER(Shape), ctypes.POINTER(KV)
+    sig = {
+        "hylra_workspace_size": [SP, I32, ctypes.POINTER(SZ)],
+        "hylra_decode_full": [SP, P, KP, P, P, P, P, SZ, P],
+        "hylra_block_topk": [SP, P, P, I32, P, P],
+        "hylra_decode_sparse": [SP, P, KP, P, I32, P, P, P, SZ, P],
+        "hylra_run_policy": [SP, I32, P, I32, P, KP, P, P, P, P, SZ, P],
+        "hylra_policy_dp": [I32, P, ctypes.c_float, P, P, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int32
+    lib.hylra_status_str.argtypes = [ctypes.c_int32]
+    lib.hylra_status_str.restype = ctypes.c_char_p
+    lib.hylra_last_error.argtypes = []
+    lib.hylra_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
+            "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_status_str",
+            "hylra_last_error")
+
+
+def _status_str(st: int) -> str:
+    return _lib.hylra_status_str(int(st)).decode()
+
+
+def last_error() -> str:
+    return _lib.hylra_last_error().decode()
+
+
+def _check(st: int):
+    if st != OK:
+        raise HylraError(st, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, cuda=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if cuda and not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s has dtype %s" % (name, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, has shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def make_shape(q: torch.Tensor, k_pool: torch.Tensor, table: torch.Tensor, scale: float = 0.0) -> Shape:
+    _need(q, "q", tuple(_DTYPES), 3)
+    _need(k_pool, "k_pool", q.dtype, 4)
+    _need(table, "block_table", torch.int32, 2)
+    B, Hq, d = q.shape
+    return Shape(B, Hq, k_pool.shape[1], d, BLOCK, _DTYPES[q.dtype], table.shape[1], float(scale))
+
+
+def make_kv(k_pool, v_pool, table, ctx) -> KV:
+    _need(k_pool, "k_pool", tuple(_DTYPES), 4)
+    _need(v_pool, "v_pool", k_pool.dtype, 4)
+    _need(table, "block_table", torch.int32, 2)
+    _need(ctx, "ctx_lens", torch.int32, 1)
+    P, Hkv, blk, d = k_pool.shape
+    if blk != BLOCK or tuple(v_pool.shape) != (P, Hkv, d, BLOCK):
+        raise ValueError("K pool must be [pages][Hkv][128][d] and V pool [pages][Hkv][d][128]")
+    if ctx.shape[0] != table.shape[0]:
+        raise ValueError("ctx_lens and block_table disagree on the batch size")
+    return KV(k_pool.data_ptr(), v_pool.data_ptr(), P, table.data_ptr(), ctx.data_ptr())
+
+
+def workspace_size(shape: Shape, k: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.hylra_workspace_size(ctypes.byref(shape), int(k), ctypes.byref(n)))
+    return int(n.value)
+
+
+_ws_cache = {}
+
+
+def workspace(shape: Shape, k: int, device) -> torch.Tensor:
+    """A cached device workspace big enough for `shape` and `k` (one per device)."""
+    need = workspace_size(shape, k)
+    dev = torch.device(device)
+    key = (dev.type, dev.index)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def decode_full(q, k_pool, v_pool, table, ctx, *, scale=0.0, want_scores=False, out=None,
+                lse=None, block_score=None, ws=None, stream=None):
+    """Full decode attention of one layer; returns (out, lse, block_score or None)."""
+    shape = make_shape(q, k_pool, table, scale)
+    kv = make_kv(k_pool, v_pool, table, ctx)
+    B, Hq, d = q.shape
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device) if out is None else out
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if lse is None else lse
+    if want_scores and block_score is None:
+        block_score = torch.empty(B, shape.num_kv_heads, shape.max_blocks_per_seq,
+                                  dtype=torch.float32, device=q.device)
+    ws = workspace(shape, 0, q.device) if ws is None else ws
+    _check(_lib.hylra_decode_full(ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(out),
+                                  _ptr(lse), _ptr(block_score), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return out, lse, block_score
+
+
+def block_topk(block_score, ctx, k, *, idx=None, stream=None):
+    """Top-k block ids of a [B][Hkv][max_blocks] float32 score array."""
+    _need(block_score, "block_score", torch.float32, 3)
+    _need(ctx, "ctx_lens", torch.int32, 1)
+    B, Hkv, mb = block_score.shape
+    shape = Shape(B, Hkv, Hkv, 128, BLOCK, BF16, mb, 0.0)
+    idx = torch.empty(B, Hkv, int(k), dtype=torch.int32, device=block_score.device) \
+        if idx is None else idx
+    _check(_lib.hylra_block_topk(ctypes.byref(shape), _ptr(block_score), _ptr(ctx), int(k),
+                                 _ptr(idx), _stream(stream)))
+    return idx
+
+
+def decode_sparse(q, k_pool, v_pool, table, ctx, idx, *, scale=0.0, out=None, lse=None,
+                  ws=None, stream=None):
+    """Decode attention restricted to the blocks in idx [B][Hkv][k]; returns (out, lse)."""
+    shape = make_shape(q, k_pool, table, scale)
+    kv = make_kv(k_pool, v_pool, table, ctx)
+    _need(idx, "idx", torch.int32, 3)
+    k = idx.shape[2]
+    B, Hq, d = q.shape
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device) if out is None else out
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if lse is None else lse
+    ws = workspace(shape, k, q.device) if ws is None else ws
+    _check(_lib.hylra_decode_sparse(ctypes.byref(shape), _ptr(q), ctypes.byref(kv), _ptr(idx),
+                                    int(k), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+    return out, lse
+
+
+class PolicyPlan:
+    """Pre-marshalled arguments of hylra_run_policy for a fixed set of layer
+    tensors, so that repeated decode steps pay no Python marshalling."""
+
+    def __init__(self, layers: Sequence[dict], src: Sequence[int], k: int, *, scale=0.0,
+                 outs=None, lses=None, idx_log=None, ws=None):
+        first = layers[0]
+        self.shape = make_shape(first["q"], first["k_pool"], first["table"], scale)
+        L = len(layers)
+        self.L = L
+        self.k = int(k)
+        B, Hq, d = first["q"].shape
+        dev = first["q"].device
+        self.src = (ctypes.c_int32 * L)(*[int(s) for s in src])
+        self.kvs = (KV * L)(*[make_kv(l["k_pool"], l["v_pool"], l["table"], l["ctx"])
+                              for l in layers])
+        for l in layers:
+            _need(l["q"], "q", first["q"].dtype, 3)
+        self.qs = (ctypes.c_void_p * L)(*[l["q"].data_ptr() for l in layers])
+        self.out = outs if outs is not None else [
+            torch.empty(B, Hq, d, dtype=torch.float32, device=dev) for _ in range(L)]
+        self.lse = lses if lses is not None else [
+            torch.empty(B, Hq, dtype=torch.float32, device=dev) for _ in range(L)]
+        self.outs = (ctypes.c_void_p * L)(*[o.data_ptr() for o in self.out])
+        self.lses = (ctypes.c_void_p * L)(*[o.data_ptr() for o in self.lse])
+        self.idx_log = idx_log
+        self.ws = workspace(self.shape, self.k, dev) if ws is None else ws
+        self._layers = layers  # keep tensors alive
+
+    def run(self, stream=None):
+        _check(_lib.hylra_run_policy(ctypes.byref(self.shape), self.L, self.src, self.k,
+                                     self.qs, self.kvs, self.outs, self.lses,
+                                     _ptr(self.idx_log), _ptr(self.ws), self.ws.numel(),
+                                     _stream(stream)))
+        return self.out, self.lse
+
+
+def run_policy(layers, src, k, *, scale=0.0, idx_log=None, ws=None, stream=None):
+    """One hybrid decode step over the layers (list of dicts with q, k_pool,
+    v_pool, table, ctx).  Returns (outs, lses, idx_log)."""
+    if idx_log is None:
+        first = layers[0]
+        B = first["q"].shape[0]
+        idx_log = torch.full((len(layers), B, first["k_pool"].shape[1], int(k)), -2,
+                             dtype=torch.int32, device=first["q"].device)
+    plan = PolicyPlan(layers, src, k, scale=scale, idx_log=idx_log, ws=ws)
+    outs, lses = plan.run(stream)
+    return outs, lses, idx_log
+
+
+def policy_dp(M, theta: float, force=None):
+    """Offline policy DP on the host (row = target, column = source).
+    Returns (src list, num_resets, sim_sum)."""
+    M = np.ascontiguousarray(np.asarray(M, dtype=np.float32))
+    L = M.shape[0]
+    if M.shape != (L, L):
+        raise ValueError("M must be square")
+    f = None
+    if force is not None:
+        f = np.ascontiguousarray(np.asarray(force, dtype=np.uint8))
+        if f.shape != (L,):
+            raise ValueError("force must have one entry per layer")
+    src = np.zeros(L, np.int32)
+    nres = ctypes.c_int32(0)
+    sim = ctypes.c_double(0.0)
+    _check(_lib.hylra_policy_dp(L, M.ctypes.data_as(ctypes.c_void_p), ctypes.c_float(theta),
+                                None if f is None else f.ctypes.data_as(ctypes.c_void_p),
+                                src.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nres),
+                                ctypes.byref(sim)))
+    return src.tolist(), int(nres.value), float(sim.value)

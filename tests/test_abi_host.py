@@ -1,0 +1,192 @@
+"""Host-side checks of the C-ABI library (no GPU work is launched here):
+the library loads, exports every symbol the header declares, validates its
+arguments before touching the device, and its host policy DP agrees with the
+oracle's DP and with brute force."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_layer_reuse_amd import hylra as H
+from sparse_layer_reuse_amd import synth, workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "hylra.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|hylra_status)\s*(hylra_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 8, names
+    lib = ctypes.CDLL(H.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(H.EXPORTED)
+
+
+def test_status_strings():
+    for st in range(6):
+        assert H._status_str(st)
+    assert H._status_str(99) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def _kv(**over):
+    kv = H.KV(0x10000, 0x20000, 4, 0x30000, 0x40000)
+    for k, v in over.items():
+        setattr(kv, k, v)
+    return kv
+
+
+def _shape(**over):
+    s = H.Shape(2, 8, 2, 128, 128, H.BF16, 16, 0.0)
+    for k, v in over.items():
+        setattr(s, k, v)
+    return s
+
+
+def _full(shape, kv=None, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    kv = _kv() if kv is None else kv
+    return H._lib.hylra_decode_full(ctypes.byref(shape), q, ctypes.byref(kv), out, None, None,
+                                    ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(batch=0), H.E_INVALID_ARG),
+    (dict(num_kv_heads=0), H.E_INVALID_ARG),
+    (dict(num_q_heads=6, num_kv_heads=4), H.E_INVALID_ARG),
+    (dict(num_q_heads=34, num_kv_heads=2), H.E_UNSUPPORTED),
+    (dict(head_dim=96), H.E_UNSUPPORTED),
+    (dict(block_size=64), H.E_UNSUPPORTED),
+    (dict(dtype=7), H.E_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), H.E_UNSUPPORTED),
+    (dict(max_blocks_per_seq=8193), H.E_UNSUPPORTED),
+    (dict(scale=float("nan")), H.E_INVALID_ARG),
+    (dict(scale=-1.0), H.E_INVALID_ARG),
+])
+def test_shape_validation(over, status):
+    assert _full(_shape(**over)) == status
+    assert H.last_error()
+
+
+def test_pointer_and_workspace_validation():
+    s = _shape()
+    assert _full(s, q=None) == H.E_INVALID_ARG
+    assert _full(s, out=None) == H.E_INVALID_ARG
+    assert _full(s, q=ctypes.c_void_p(0x10004)) == H.E_INVALID_ARG  # misaligned
+    assert _full(s, kv=_kv(k_pool=None)) == H.E_INVALID_ARG
+    assert _full(s, kv=_kv(num_pages=0)) == H.E_INVALID_ARG
+    assert _full(s, kv=_kv(v_pool=0x20008)) == H.E_INVALID_ARG
+    assert _full(s, ws=None) == H.E_WORKSPACE
+    need = H.workspace_size(s, 0)
+    assert _full(s, ws_bytes=need - 1) == H.E_WORKSPACE
+    assert str(need) in H.last_error()
+    # sparse / top-k specific
+    kv = _kv()
+    assert H._lib.hylra_decode_sparse(ctypes.byref(s), FAKE, ctypes.byref(kv), FAKE, 0, FAKE,
+                                      None, FAKE, 1 << 30, None) == H.E_INVALID_ARG
+    assert H._lib.hylra_decode_sparse(ctypes.byref(s), FAKE, ctypes.byref(kv), None, 4, FAKE,
+                                      None, FAKE, 1 << 30, None) == H.E_INVALID_ARG
+    assert H._lib.hylra_block_topk(ctypes.byref(s), FAKE, FAKE, 0, FAKE, None) == H.E_INVALID_ARG
+    assert H._lib.hylra_block_topk(ctypes.byref(s), None, FAKE, 2, FAKE, None) == H.E_INVALID_ARG
+
+
+def _run_policy(src, k=4, L=None, kvs=None, q_ok=True):
+    L = len(src) if L is None else L
+    s = _shape()
+    srcs = (ctypes.c_int32 * len(src))(*src)
+    kvs = (H.KV * L)(*[_kv() for _ in range(L)]) if kvs is None else kvs
+    qs = (ctypes.c_void_p * L)(*([0x10000] * L if q_ok else [0] * L))
+    outs = (ctypes.c_void_p * L)(*([0x50000] * L))
+    return H._lib.hylra_run_policy(ctypes.byref(s), L, srcs, k, qs, kvs, outs, None, None,
+                                   FAKE, 1 << 30, None)
+
+
+@pytest.mark.parametrize("src", [[1, 1], [0, 2, 2], [0, 1, 0], [0, 0, 1], [0, 1, 1, 0]])
+def test_run_policy_rejects_malformed_policy(src):
+    assert _run_policy(src) == H.E_BAD_POLICY
+    assert not oracle.check_policy(src)
+
+
+def test_run_policy_argument_checks():
+    assert _run_policy([0, 0], k=0) == H.E_INVALID_ARG
+    assert _run_policy([0, 0], q_ok=False) == H.E_INVALID_ARG
+    bad = (H.KV * 2)(_kv(), _kv(block_table=None))
+    assert _run_policy([0, 0], kvs=bad) == H.E_INVALID_ARG
+    assert "layer 1" in H.last_error()
+
+
+def test_workspace_size_grows_with_k_and_context():
+    s = _shape()
+    a = H.workspace_size(s, 4)
+    b = H.workspace_size(_shape(max_blocks_per_seq=64), 4)
+    c = H.workspace_size(s, 16)
+    assert 0 < a < b and a <= c
+    for wl in W.ALL.values():
+        sh = H.Shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 128,
+                     H.F32 if wl.dtype == "f32" else H.BF16, wl.blocks, 0.0)
+        # workspace stays a small fraction of one layer's KV
+        assert H.workspace_size(sh, max(wl.topk)) < 0.1 * wl.kv_bytes_per_layer()
+
+
+def test_policy_dp_argument_checks():
+    M = np.zeros((3, 3), np.float32)
+    with pytest.raises(H.HylraError):
+        H.policy_dp(np.zeros((0, 0), np.float32), 0.5)
+    with pytest.raises(H.HylraError):
+        H.policy_dp(M, float("nan"))
+    Mn = M.copy()
+    Mn[2, 0] = np.nan
+    with pytest.raises(H.HylraError):
+        H.policy_dp(Mn, 0.5)
+
+
+def test_policy_dp_matches_oracle_and_bruteforce():
+    rng = np.random.default_rng(123)
+    for trial in range(300):
+        L = int(rng.integers(1, 13))
+        decay = float(rng.choice([3.0, 6.0, 10.0]))
+        M = synth.similarity_matrix(L, decay, seed=int(rng.integers(1 << 30)))
+        if trial % 3 == 0:  # quantised entries: many exact ties
+            M = (np.round(M * 4) / 4).astype(np.float32)
+        theta = float(np.float32(rng.choice([0.2, 0.5, 0.7, 0.8, 0.9])))
+        force = (rng.random(L) < 0.2).tolist()
+        got = H.policy_dp(M, theta, force)
+        want = oracle.brute_force_policy(M, theta, force)
+        assert got[0] == want[0], (L, theta, force)
+        assert got[1] == want[1]
+        assert abs(got[2] - want[2]) < 1e-9
+
+
+def test_policy_dp_workloads_match_oracle():
+    for wl in (W.LLAMA3_8B_B8_64K_DP, W.LLAMA3_70B_128K_DP):
+        M = synth.workload_similarity(wl)
+        force = [j in wl.dp_force for j in range(wl.layers)]
+        for theta in wl.dp_theta:
+            got = H.policy_dp(M, theta, force)
+            want = oracle.policy_dp(M, theta, force)
+            assert got[0] == want[0] and got[1] == want[1]
+            assert abs(got[2] - want[2]) < 1e-9
+
+
+def test_policy_dp_golden():
+    import json
+    spec = json.load(open(os.path.join(ROOT, "tests", "golden", "policy_worked.json")))
+    L = spec["L"]
+    M = np.zeros((L, L), np.float32)
+    for key, val in spec["M_lower"].items():
+        j, i = map(int, key.split(","))
+        M[j, i] = np.float32(val)
+    for case in spec["cases"]:
+        force = [j in case["force"] for j in range(L)]
+        src, r, _ = H.policy_dp(M, float(np.float32(case["theta"])), force)
+        assert src == case["src"] and r == case["resets"], case
