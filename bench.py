@@ -1,0 +1,222 @@
+"""Decode-attention benchmark of the hybrid layer-reuse policy on one MI355X.
+
+A step is one hybrid decode step of every layer of the workload (reset layers:
+full attention + block scores + top-k; reuse layers: attention over the
+carried blocks) for the whole batch, inputs resident in HBM.  Also timed: the
+plain full-attention step (every layer full attention, no scores) and the
+all-reset step (every layer full attention + scores + top-k).
+
+Prints one JSON line.  `value` is hybrid decode steps/s.  `roofline` covers
+the dominant kernel (full split attention of the reset layers): algorithmic
+bytes per launch = 4*B*Hkv*T*d (bf16 K and V, each read once), divided by its
+average launch time from HIP events recorded on the launch stream during the
+timed hybrid steps.  `cpu_baseline` times the CPU oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn steps/s @32K-128K ctx; achieved HBM GB/s vs peak; hybrid/full speedup"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama3_8b_32k")
+    p.add_argument("--topk", type=int, default=None)
+    p.add_argument("--theta", type=float, default=None)
+    p.add_argument("--layers", type=int, default=None, help="use only the first N layers")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="budget of the CPU oracle baseline (0 disables it)")
+    p.add_argument("--skip-baselines", action="store_true",
+                   help="time only the hybrid step (for short profiler runs)")
+    return p.parse_args()
+
+
+def policy_for(wl, hylra, theta, L):
+    from sparse_layer_reuse_amd import synth, workloads as W
+    if wl.policy == "fixed":
+        src = W.src_from_resets(wl.layers, wl.resets)
+        desc = "fixed resets %s" % (list(wl.resets),)
+        theta = None
+    else:
+        theta = wl.dp_theta[0] if theta is None else theta
+        M = synth.workload_similarity(wl)
+        force = [j in wl.dp_force for j in range(wl.layers)]
+        src, _, _ = hylra.policy_dp(M, theta, force)
+        desc = "dp theta=%g decay=%g force=%s" % (theta, wl.dp_decay, list(wl.dp_force))
+    src = src[:L]
+    return src, desc, theta
+
+
+def timed(fn, steps, warmup, torch, timers, hylra):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    for kind in timers:
+        hylra.timer_start(kind, capacity=max(64, steps * 128))
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    kern = {}
+    for kind in timers:
+        tot, n = hylra.timer_stop(kind)
+        kern[kind] = (tot / n if n else None, n)
+    return ms, kern
+
+
+def cpu_baseline(wl, layers, src, k, budget_s):
+    """Oracle timed on the host over a prefix of the step's layers; the step
+    time is extrapolated from the mean reset-layer and reuse-layer times."""
+    import oracle
+    from sparse_layer_reuse_amd import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    t_reset, t_reuse = [], []
+    carried = None
+    t_start = time.time()
+    for j, lay in enumerate(layers):
+        o = synth.layer_to_oracle(lay)
+        t0 = time.perf_counter()
+        if src[j] == j:
+            _, _, score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
+                                             o["ctx"], num_kv_heads=wl.num_kv_heads)
+            carried, _ = oracle.topk(score, o["ctx"], k)
+            t_reset.append(time.perf_counter() - t0)
+        else:
+            oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
+                          num_kv_heads=wl.num_kv_heads, sel=carried, k=k)
+            t_reuse.append(time.perf_counter() - t0)
+        del o
+        if time.time() - t_start > budget_s and t_reset and (t_reuse or j + 1 == len(layers)):
+            break
+    n_reset = sum(1 for j, s in enumerate(src) if s == j)
+    n_reuse = len(src) - n_reset
+    mean = lambda v: sum(v) / len(v) if v else 0.0
+    step_s = n_reset * mean(t_reset) + n_reuse * mean(t_reuse)
+    measured = len(t_reset) + len(t_reuse)
+    return {
+        "value": 1.0 / step_s if step_s > 0 else None,
+        "unit": "steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "layers 0-%d of the hybrid step (%d reset, %d reuse) timed, step time "
+                  "extrapolated to %d reset + %d reuse layers; float64 C oracle, OpenMP"
+                  % (measured - 1, len(t_reset), len(t_reuse), n_reset, n_reuse),
+        "reset_layer_s": mean(t_reset),
+        "reuse_layer_s": mean(t_reuse),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_layer_reuse_amd import hylra, synth, workloads as W
+
+    wl = W.get(args.workload)
+    k = args.topk or wl.topk[0]
+    L = min(wl.layers, args.layers or wl.layers)
+    t0 = time.time()
+    layers = synth.workload_layers(wl, device="cuda", layers=range(L))
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    src, policy_desc, theta = policy_for(wl, hylra, args.theta, L)
+    n_reset = sum(1 for j, s in enumerate(src) if s == j)
+
+    hybrid = hylra.PolicyPlan(layers, src, k)
+    ALL = (hylra.KERNEL_FULL_ATTN, hylra.KERNEL_SPARSE_ATTN, hylra.KERNEL_MERGE,
+           hylra.KERNEL_TOPK)
+    ms_h, kern = timed(hybrid.run, args.steps, args.warmup, torch, ALL, hylra)
+    result_extra = {}
+    if not args.skip_baselines:
+        full = hylra.FullPlan(layers)
+        ms_f, kern_f = timed(full.run, args.steps, args.warmup, torch,
+                             (hylra.KERNEL_FULL_ATTN, hylra.KERNEL_MERGE), hylra)
+        allreset = hylra.PolicyPlan(layers, list(range(L)), k)
+        ms_a, _ = timed(allreset.run, args.steps, args.warmup, torch, (), hylra)
+        result_extra = {
+            "full_steps_per_s": 1000.0 / ms_f,
+            "full_ms_per_step": ms_f,
+            "all_reset_steps_per_s": 1000.0 / ms_a,
+            "hybrid_over_full": ms_f / ms_h,
+            "full_attn_no_scores_us": kern_f[hylra.KERNEL_FULL_ATTN][0] * 1e3,
+        }
+
+    B, Hkv, T, d = wl.batch, wl.num_kv_heads, wl.ctx, wl.head_dim
+    elt = 4 if wl.dtype == "f32" else 2
+    full_bytes = 2 * B * Hkv * T * d * elt          # K and V of every token, once
+    sparse_bytes = 2 * B * Hkv * min(k, wl.blocks) * 128 * d * elt
+    us = lambda kind: (kern[kind][0] * 1e3) if kern[kind][0] is not None else None
+    full_us, sparse_us = us(hylra.KERNEL_FULL_ATTN), us(hylra.KERNEL_SPARSE_ATTN)
+    merge_us, topk_us = us(hylra.KERNEL_MERGE), us(hylra.KERNEL_TOPK)
+    achieved = full_bytes / (full_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / ms_h,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_h,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V with planted hot blocks; no trained weights)",
+        "config": {
+            "workload": wl.name, "batch": B, "layers": L, "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": Hkv, "head_dim": d, "ctx": T, "block": 128, "topk": k,
+            "paged": wl.paged, "policy": policy_desc, "resets": n_reset, "reuses": L - n_reset,
+        },
+        "per_layer_us": {
+            "reset_layer": (full_us or 0) + (merge_us or 0) + (topk_us or 0),
+            "reuse_layer": ((sparse_us or 0) + (merge_us or 0)) if sparse_us else None,
+            "wall_avg": ms_h * 1e3 / L,
+        },
+        "kernels_us": {hylra.KERNEL_NAMES[kk]: us(kk) for kk in ALL},
+        "kernel_launches": {hylra.KERNEL_NAMES[kk]: kern[kk][1] for kk in ALL},
+        "sparse_attn_gbs": (sparse_bytes / (sparse_us * 1e-6) / 1e9) if sparse_us else None,
+        "roofline": {
+            "kernel": "attn_split_bf16<128> (full, reset layers)" if wl.dtype == "bf16"
+                      else "attn_split_f32 (full, reset layers)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": full_bytes,
+            "avg_launch_us": full_us,
+        },
+        "input_generation_s": gen_s,
+    }
+    out.update(result_extra)
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, layers, src, k, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

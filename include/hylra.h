@@ -139,6 +139,19 @@ hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
                              const uint8_t *force_reset, int32_t *src_out, int32_t *num_resets,
                              double *sim_sum);
 
+/* Kernel timer (instrumentation).  While the timer of a kernel kind runs,
+ * every launch of that kind is bracketed by a pair of HIP events recorded on
+ * the launch stream (the first `capacity` launches).  hylra_timer_stop waits
+ * for the recorded events and returns the summed kernel time in milliseconds
+ * and the number of timed launches (both pointers nullable).  Timers are
+ * process-global and not thread-safe; starting a running timer restarts it. */
+#define HYLRA_KERNEL_FULL_ATTN 0   /* split attention over every block (reset layers) */
+#define HYLRA_KERNEL_SPARSE_ATTN 1 /* split attention over selected blocks (reuse layers) */
+#define HYLRA_KERNEL_MERGE 2       /* split merge: out, lse, per-head block mass */
+#define HYLRA_KERNEL_TOPK 3        /* block score and top-k selection */
+hylra_status hylra_timer_start(int32_t kind, int32_t capacity);
+hylra_status hylra_timer_stop(int32_t kind, double *total_ms, int32_t *launches);
+
 /* Static string for a status code. */
 const char *hylra_status_str(hylra_status status);
 

@@ -415,6 +415,22 @@ hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
   return ok();
 }
 
+hylra_status hylra_timer_start(int32_t kind, int32_t capacity) {
+  if (kind < 0 || kind >= hylra::kNumTimers) return fail(HYLRA_E_INVALID_ARG, "unknown timer kind %d", kind);
+  if (capacity < 1 || capacity > (1 << 20))
+    return fail(HYLRA_E_INVALID_ARG, "timer capacity must be in [1, 2^20] (got %d)", capacity);
+  if (hylra_status st = device_status(hylra::timer_start(kind, capacity), "timer start")) return st;
+  return ok();
+}
+
+hylra_status hylra_timer_stop(int32_t kind, double *total_ms, int32_t *launches) {
+  if (kind < 0 || kind >= hylra::kNumTimers) return fail(HYLRA_E_INVALID_ARG, "unknown timer kind %d", kind);
+  int n = 0;
+  if (hylra_status st = device_status(hylra::timer_stop(kind, total_ms, &n), "timer stop")) return st;
+  if (launches) *launches = n;
+  return ok();
+}
+
 const char *hylra_status_str(hylra_status status) {
   switch (status) {
     case HYLRA_OK: return "ok";

@@ -83,4 +83,10 @@ int launch_merge(const MergeArgs &a, int batch, void *stream);
 int launch_topk(const TopkArgs &a, int batch, void *stream);
 const char *device_error_string(int code);
 
+// Kernel timers (see hylra_timer_start in hylra.h).
+enum TimerKind { kTimerFullAttn = 0, kTimerSparseAttn = 1, kTimerMerge = 2, kTimerTopk = 3,
+                 kNumTimers = 4 };
+int timer_start(int kind, int capacity);
+int timer_stop(int kind, double *total_ms, int *launches);
+
 }  // namespace hylra

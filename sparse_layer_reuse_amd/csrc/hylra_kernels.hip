@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "hylra_internal.h"
 
 namespace hylra {
@@ -619,11 +621,71 @@ __global__ __launch_bounds__(kThreads) void score_topk(TopkArgs a) {
   for (int r = keff + threadIdx.x; r < a.k; r += kThreads) out[r] = -1;
 }
 
+// Kernel timers: event pairs recorded around launches while running.
+struct KernelTimer {
+  bool running = false;
+  int recorded = 0;
+  std::vector<hipEvent_t> start, stop;
+};
+KernelTimer g_timers[kNumTimers];
+
+struct TimerScope {
+  KernelTimer *t;
+  hipStream_t st;
+  bool on;
+  TimerScope(int kind, hipStream_t s) : t(&g_timers[kind]), st(s) {
+    on = t->running && t->recorded < (int)t->start.size();
+    if (on) (void)hipEventRecord(t->start[t->recorded], st);
+  }
+  ~TimerScope() {
+    if (on) (void)hipEventRecord(t->stop[t->recorded++], st);
+  }
+};
+
 }  // namespace
+
+int timer_start(int kind, int capacity) {
+  KernelTimer &t = g_timers[kind];
+  hipError_t err = hipSuccess;
+  while ((int)t.start.size() < capacity && err == hipSuccess) {
+    hipEvent_t a, b;
+    err = hipEventCreate(&a);
+    if (err != hipSuccess) break;
+    err = hipEventCreate(&b);
+    if (err != hipSuccess) {
+      (void)hipEventDestroy(a);
+      break;
+    }
+    t.start.push_back(a);
+    t.stop.push_back(b);
+  }
+  t.recorded = 0;
+  t.running = err == hipSuccess;
+  return (int)err;
+}
+
+int timer_stop(int kind, double *total_ms, int *launches) {
+  KernelTimer &t = g_timers[kind];
+  t.running = false;
+  double sum = 0.0;
+  for (int i = 0; i < t.recorded; ++i) {
+    hipError_t err = hipEventSynchronize(t.stop[i]);
+    if (err != hipSuccess) return (int)err;
+    float ms = 0.f;
+    err = hipEventElapsedTime(&ms, t.start[i], t.stop[i]);
+    if (err != hipSuccess) return (int)err;
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = t.recorded;
+  t.recorded = 0;
+  return 0;
+}
 
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream) {
   const dim3 grid(a.nsplit, a.num_kv_heads, batch);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  TimerScope timer(a.sel == nullptr ? kTimerFullAttn : kTimerSparseAttn, st);
   if (dtype == 1) {
     if (head_dim == 128) hipLaunchKernelGGL(attn_split_bf16<128>, grid, dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL(attn_split_bf16<64>, grid, dim3(kThreads), 0, st, a);
@@ -635,12 +697,14 @@ int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *str
 }
 
 int launch_merge(const MergeArgs &a, int batch, void *stream) {
+  TimerScope timer(kTimerMerge, static_cast<hipStream_t>(stream));
   hipLaunchKernelGGL(merge_heads, dim3(a.num_q_heads, batch), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 
 int launch_topk(const TopkArgs &a, int batch, void *stream) {
+  TimerScope timer(kTimerTopk, static_cast<hipStream_t>(stream));
   hipLaunchKernelGGL(score_topk, dim3(a.num_kv_heads, batch), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();

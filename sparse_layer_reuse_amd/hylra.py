@@ -57,6 +57,8 @@ def _load():
         "hylra_decode_sparse": [SP, P, KP, P, I32, P, P, P, SZ, P],
         "hylra_run_policy": [SP, I32, P, I32, P, KP, P, P, P, P, SZ, P],
         "hylra_policy_dp": [I32, P, ctypes.c_float, P, P, P, P],
+        "hylra_timer_start": [I32, I32],
+        "hylra_timer_stop": [I32, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -72,8 +74,12 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
-            "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_status_str",
-            "hylra_last_error")
+            "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_timer_start",
+            "hylra_timer_stop", "hylra_status_str", "hylra_last_error")
+
+KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_MERGE, KERNEL_TOPK = range(4)
+KERNEL_NAMES = {KERNEL_FULL_ATTN: "attn_split_full", KERNEL_SPARSE_ATTN: "attn_split_sparse",
+                KERNEL_MERGE: "merge_heads", KERNEL_TOPK: "score_topk"}
 
 
 def _status_str(st: int) -> str:
@@ -277,3 +283,42 @@ def policy_dp(M, theta: float, force=None):
                                 src.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nres),
                                 ctypes.byref(sim)))
     return src.tolist(), int(nres.value), float(sim.value)
+
+
+def timer_start(kind: int, capacity: int = 4096) -> None:
+    """Start bracketing every launch of a kernel kind with HIP events."""
+    _check(_lib.hylra_timer_start(int(kind), int(capacity)))
+
+
+def timer_stop(kind: int):
+    """Stop a kernel timer; returns (summed kernel milliseconds, launches)."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    _check(_lib.hylra_timer_stop(int(kind), ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
+
+
+class FullPlan:
+    """Pre-marshalled hylra_decode_full calls over a list of layers (no block
+    scores): the plain full-attention step used as the baseline policy."""
+
+    def __init__(self, layers, *, scale=0.0, ws=None):
+        first = layers[0]
+        self.shape = make_shape(first["q"], first["k_pool"], first["table"], scale)
+        B, Hq, d = first["q"].shape
+        dev = first["q"].device
+        self.kvs = [make_kv(l["k_pool"], l["v_pool"], l["table"], l["ctx"]) for l in layers]
+        self.qs = [ctypes.c_void_p(l["q"].data_ptr()) for l in layers]
+        self.out = [torch.empty(B, Hq, d, dtype=torch.float32, device=dev) for _ in layers]
+        self.lse = [torch.empty(B, Hq, dtype=torch.float32, device=dev) for _ in layers]
+        self.ws = workspace(self.shape, 0, dev) if ws is None else ws
+        self._args = [(ctypes.byref(self.shape), q, ctypes.byref(kv), _ptr(o), _ptr(l), None,
+                       _ptr(self.ws), self.ws.numel()) for q, kv, o, l in
+                      zip(self.qs, self.kvs, self.out, self.lse)]
+        self._layers = layers
+
+    def run(self, stream=None):
+        st = _stream(stream)
+        for a in self._args:
+            _check(_lib.hylra_decode_full(*a, st))
+        return self.out, self.lse
