@@ -144,14 +144,13 @@ def main():
     n_reset = sum(1 for j, s in enumerate(src) if s == j)
 
     hybrid = hylra.PolicyPlan(layers, src, k)
-    ALL = (hylra.KERNEL_FULL_ATTN, hylra.KERNEL_SPARSE_ATTN, hylra.KERNEL_MERGE,
-           hylra.KERNEL_TOPK)
+    ALL = (hylra.KERNEL_FULL_ATTN, hylra.KERNEL_SPARSE_ATTN)
     ms_h, kern = timed(hybrid.run, args.steps, args.warmup, torch, ALL, hylra)
     result_extra = {}
     if not args.skip_baselines:
         full = hylra.FullPlan(layers)
         ms_f, kern_f = timed(full.run, args.steps, args.warmup, torch,
-                             (hylra.KERNEL_FULL_ATTN, hylra.KERNEL_MERGE), hylra)
+                             (hylra.KERNEL_FULL_ATTN,), hylra)
         allreset = hylra.PolicyPlan(layers, list(range(L)), k)
         ms_a, _ = timed(allreset.run, args.steps, args.warmup, torch, (), hylra)
         result_extra = {
@@ -168,7 +167,6 @@ def main():
     sparse_bytes = 2 * B * Hkv * min(k, wl.blocks) * 128 * d * elt
     us = lambda kind: (kern[kind][0] * 1e3) if kern[kind][0] is not None else None
     full_us, sparse_us = us(hylra.KERNEL_FULL_ATTN), us(hylra.KERNEL_SPARSE_ATTN)
-    merge_us, topk_us = us(hylra.KERNEL_MERGE), us(hylra.KERNEL_TOPK)
     achieved = full_bytes / (full_us * 1e-6) / 1e9
     out = {
         "metric": METRIC,
@@ -189,16 +187,16 @@ def main():
             "paged": wl.paged, "policy": policy_desc, "resets": n_reset, "reuses": L - n_reset,
         },
         "per_layer_us": {
-            "reset_layer": (full_us or 0) + (merge_us or 0) + (topk_us or 0),
-            "reuse_layer": ((sparse_us or 0) + (merge_us or 0)) if sparse_us else None,
+            "reset_layer": full_us,
+            "reuse_layer": sparse_us,
             "wall_avg": ms_h * 1e3 / L,
         },
         "kernels_us": {hylra.KERNEL_NAMES[kk]: us(kk) for kk in ALL},
         "kernel_launches": {hylra.KERNEL_NAMES[kk]: kern[kk][1] for kk in ALL},
         "sparse_attn_gbs": (sparse_bytes / (sparse_us * 1e-6) / 1e9) if sparse_us else None,
         "roofline": {
-            "kernel": "attn_split_bf16<128> (full, reset layers)" if wl.dtype == "bf16"
-                      else "attn_split_f32 (full, reset layers)",
+            "kernel": ("attn_split_bf16<%d>" if wl.dtype == "bf16" else "attn_split_f32<%d>")
+                      % d + " full mode (reset layer: split pass + fused merge/score/top-k)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

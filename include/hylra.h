@@ -60,7 +60,7 @@ typedef int32_t hylra_status;
 #define HYLRA_BLOCK_TOKENS 128
 
 typedef struct {
-  int32_t batch;              /* B >= 1 */
+  int32_t batch;              /* B >= 1; B * num_kv_heads <= 65536 */
   int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;       /* Hkv >= 1 */
   int32_t head_dim;           /* d: 64 or 128 */
@@ -80,7 +80,10 @@ typedef struct {
 
 /* Bytes of device workspace that every entry point below needs for `shape`
  * and top-k `k` (k <= 0 allowed when no sparse/top-k call is made).  The
- * caller allocates it once and may reuse it across calls on one stream. */
+ * caller allocates it once, zero-fills it before its first use, and may reuse
+ * it across calls on one stream: it holds per-(sequence, KV head) arrival
+ * counters that every launch leaves at zero when it completes.  Calls that
+ * share one workspace must not overlap (use one workspace per stream). */
 hylra_status hylra_workspace_size(const hylra_shape *shape, int32_t k, size_t *bytes);
 
 /* Full decode attention of one layer (section 2.3, sensitive layers):
@@ -145,10 +148,9 @@ hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
  * for the recorded events and returns the summed kernel time in milliseconds
  * and the number of timed launches (both pointers nullable).  Timers are
  * process-global and not thread-safe; starting a running timer restarts it. */
-#define HYLRA_KERNEL_FULL_ATTN 0   /* split attention over every block (reset layers) */
-#define HYLRA_KERNEL_SPARSE_ATTN 1 /* split attention over selected blocks (reuse layers) */
-#define HYLRA_KERNEL_MERGE 2       /* split merge: out, lse, per-head block mass */
-#define HYLRA_KERNEL_TOPK 3        /* block score and top-k selection */
+#define HYLRA_KERNEL_FULL_ATTN 0   /* full attention layer: split pass + merge, scores, top-k */
+#define HYLRA_KERNEL_SPARSE_ATTN 1 /* selected-block attention layer: split pass + merge */
+#define HYLRA_KERNEL_TOPK 2        /* top-k of a given score array (hylra_block_topk) */
 hylra_status hylra_timer_start(int32_t kind, int32_t capacity);
 hylra_status hylra_timer_stop(int32_t kind, double *total_ms, int32_t *launches);
 

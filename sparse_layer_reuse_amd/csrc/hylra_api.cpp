@@ -48,8 +48,10 @@ hylra_status check_shape(const hylra_shape *s) {
   if (s->num_q_heads / s->num_kv_heads > hylra::kMaxGroup)
     return fail(HYLRA_E_UNSUPPORTED, "group size %d exceeds %d query heads per KV head",
                 s->num_q_heads / s->num_kv_heads, hylra::kMaxGroup);
-  if (s->num_kv_heads > 65535 || s->batch > 65535)
-    return fail(HYLRA_E_UNSUPPORTED, "batch and num_kv_heads must be <= 65535");
+  if (s->num_kv_heads > 65535 || s->batch > 65535 ||
+      (long)s->batch * s->num_kv_heads > hylra::kCounterSlots)
+    return fail(HYLRA_E_UNSUPPORTED, "batch and num_kv_heads must be <= 65535 and their product <= %d",
+                hylra::kCounterSlots);
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(HYLRA_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", s->head_dim);
   if (s->block_size != HYLRA_BLOCK_TOKENS)
@@ -85,7 +87,7 @@ struct Workspace {
   float *part_ml;
   float *part_o;
   float *stats;
-  float *head_mass;
+  int32_t *counters;
   int32_t *idx;
   size_t bytes;
 };
@@ -114,10 +116,12 @@ Workspace layout(const hylra_shape *s, int k, void *base) {
     off = round_up(off + bytes, a);
     return r;
   };
+  // counters first, in a fixed-size region: every shape finds them at the same
+  // place, so a workspace reused across shapes keeps them zero between calls
+  w.counters = reinterpret_cast<int32_t *>(take(hylra::kCounterSlots * sizeof(int32_t)));
   w.part_ml = reinterpret_cast<float *>(take(B * Hq * ns * 2 * sizeof(float)));
   w.part_o = reinterpret_cast<float *>(take(B * Hq * ns * D * sizeof(float)));
   w.stats = reinterpret_cast<float *>(take(B * Hq * mb * hylra::kChunksPerBlock * 2 * sizeof(float)));
-  w.head_mass = reinterpret_cast<float *>(take(B * Hq * mb * sizeof(float)));
   w.idx = reinterpret_cast<int32_t *>(take(B * Hkv * (size_t)(k > 0 ? k : 1) * sizeof(int32_t)));
   w.bytes = off;
   return w;
@@ -139,7 +143,7 @@ hylra_status device_status(int code, const char *what) {
 
 hylra::AttnArgs attn_args(const hylra_shape *s, const void *q, const hylra_kv *kv,
                           const int32_t *sel, int k, const hylra::SplitPlan &plan,
-                          const Workspace &w, bool with_stats) {
+                          const Workspace &w) {
   hylra::AttnArgs a{};
   a.q = q;
   a.k_pool = kv->k_pool;
@@ -158,104 +162,68 @@ hylra::AttnArgs attn_args(const hylra_shape *s, const void *q, const hylra_kv *k
   a.nsplit = plan.nsplit;
   a.part_ml = w.part_ml;
   a.part_o = w.part_o;
-  a.stats = with_stats ? w.stats : nullptr;
+  a.counters = w.counters;
   return a;
 }
 
-hylra::MergeArgs merge_args(const hylra::AttnArgs &a, const hylra_shape *s, float *out,
-                            float *lse, float *head_mass, int32_t *sel_log) {
-  hylra::MergeArgs m{};
-  m.part_ml = a.part_ml;
-  m.part_o = a.part_o;
-  m.stats = a.stats;
-  m.ctx = a.ctx;
-  m.sel = a.sel;
-  m.sel_log = sel_log;
-  m.k = a.k;
-  m.max_blocks = a.max_blocks;
-  m.num_q_heads = a.num_q_heads;
-  m.num_kv_heads = a.num_kv_heads;
-  m.group = a.group;
-  m.head_dim = s->head_dim;
-  m.chunks_per_wg = a.chunks_per_wg;
-  m.nsplit = a.nsplit;
-  m.out = out;
-  m.lse = lse;
-  m.head_mass = head_mass;
-  return m;
-}
-
-// Reset layer: full attention -> merge (out, lse, per-head block mass) ->
-// block score and/or top-k.
+// Reset layer: one launch -- full attention, merge, and (when asked) block
+// scores and the top-k index set.
 hylra_status run_full(const hylra_shape *s, const void *q, const hylra_kv *kv, float *out,
                       float *lse, float *block_score, int32_t *idx, int k, const Workspace &w,
                       void *stream) {
   const hylra::SplitPlan plan = hylra::plan_full(s->batch, s->num_kv_heads, s->max_blocks_per_seq);
-  const bool scores = block_score != nullptr || idx != nullptr;
-  hylra::AttnArgs a = attn_args(s, q, kv, nullptr, 0, plan, w, scores);
-  hylra_status st = device_status(hylra::launch_attn(a, s->dtype, s->head_dim, s->batch, stream),
-                                  "attention launch");
-  if (st) return st;
-  hylra::MergeArgs m = merge_args(a, s, out, lse, scores ? w.head_mass : nullptr, nullptr);
-  st = device_status(hylra::launch_merge(m, s->batch, stream), "merge launch");
-  if (st || !scores) return st;
-  hylra::TopkArgs t{};
-  t.mass = w.head_mass;
-  t.heads_per_row = s->num_q_heads / s->num_kv_heads;
-  t.ctx = kv->ctx_lens;
-  t.max_blocks = s->max_blocks_per_seq;
-  t.num_kv_heads = s->num_kv_heads;
-  t.score_out = block_score;
-  t.idx = idx;
-  t.k = k;
-  return device_status(hylra::launch_topk(t, s->batch, stream), "top-k launch");
+  hylra::AttnArgs a = attn_args(s, q, kv, nullptr, k, plan, w);
+  a.stats = (block_score != nullptr || idx != nullptr) ? w.stats : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.score_out = block_score;
+  a.idx_out = idx;
+  return device_status(hylra::launch_attn(a, s->dtype, s->head_dim, s->batch, stream),
+                       "attention launch");
 }
 
-// Reuse layer: attention over the selected blocks -> merge.
+// Reuse layer: one launch -- attention over the selected blocks and merge.
 hylra_status run_sparse(const hylra_shape *s, const void *q, const hylra_kv *kv,
                         const int32_t *idx, int k, float *out, float *lse, int32_t *log,
                         const Workspace &w, void *stream) {
   const hylra::SplitPlan plan =
       hylra::plan_sparse(s->batch, s->num_kv_heads, s->max_blocks_per_seq, k);
-  hylra::AttnArgs a = attn_args(s, q, kv, idx, k, plan, w, false);
-  hylra_status st = device_status(hylra::launch_attn(a, s->dtype, s->head_dim, s->batch, stream),
-                                  "attention launch");
-  if (st) return st;
-  hylra::MergeArgs m = merge_args(a, s, out, lse, nullptr, log);
-  return device_status(hylra::launch_merge(m, s->batch, stream), "merge launch");
+  hylra::AttnArgs a = attn_args(s, q, kv, idx, k, plan, w);
+  a.out = out;
+  a.lse = lse;
+  a.sel_log = log;
+  return device_status(hylra::launch_attn(a, s->dtype, s->head_dim, s->batch, stream),
+                       "attention launch");
 }
 
 }  // namespace
 
 namespace hylra {
 
-// Split plans: aim for about 1024 workgroups per launch (four per compute
-// unit on a 256-CU part) so the grid fills the chip at batch 1.
-constexpr long kTargetWorkgroups = 1024;
+// Split plans: about 512 workgroups per launch (two resident per compute
+// unit on a 256-CU part), each wavefront taking an equal share of chunks, and
+// at most kMaxSplits workgroups per (sequence, KV head) for the epilogue.
+constexpr long kTargetWorkgroups = 512;
 
-SplitPlan plan_full(int batch, int num_kv_heads, int max_blocks) {
-  const long C = (long)kChunksPerBlock * max_blocks;
-  const long total = (long)batch * num_kv_heads * C;
-  long cpw = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
+static SplitPlan make_plan(long chunks_per_seq, long rows) {
+  long cpw = (rows * chunks_per_seq + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  const long min_cpw = (chunks_per_seq + kMaxSplits - 1) / kMaxSplits;
+  if (cpw < min_cpw) cpw = min_cpw;
   cpw = (cpw + 3) / 4 * 4;
   if (cpw < 4) cpw = 4;
   SplitPlan p;
   p.chunks_per_wg = (int)cpw;
-  p.nsplit = (int)((C + cpw - 1) / cpw);
+  p.nsplit = (int)((chunks_per_seq + cpw - 1) / cpw);
   return p;
+}
+
+SplitPlan plan_full(int batch, int num_kv_heads, int max_blocks) {
+  return make_plan((long)kChunksPerBlock * max_blocks, (long)batch * num_kv_heads);
 }
 
 SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k) {
   const long keff = k < max_blocks ? k : max_blocks;
-  const long C = (long)kChunksPerBlock * (keff > 0 ? keff : 1);
-  const long total = (long)batch * num_kv_heads * C;
-  long cpw = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
-  if (cpw > 4) cpw = (cpw + 3) / 4 * 4;
-  if (cpw < 1) cpw = 1;
-  SplitPlan p;
-  p.chunks_per_wg = (int)cpw;
-  p.nsplit = (int)((C + cpw - 1) / cpw);
-  return p;
+  return make_plan((long)kChunksPerBlock * (keff > 0 ? keff : 1), (long)batch * num_kv_heads);
 }
 
 }  // namespace hylra
@@ -290,12 +258,10 @@ hylra_status hylra_block_topk(const hylra_shape *shape, const float *block_score
     return fail(HYLRA_E_INVALID_ARG, "block_score, ctx_lens and idx must be non-NULL");
   if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
   hylra::TopkArgs t{};
-  t.mass = block_score;
-  t.heads_per_row = 1;
+  t.score = block_score;
   t.ctx = ctx_lens;
   t.max_blocks = shape->max_blocks_per_seq;
   t.num_kv_heads = shape->num_kv_heads;
-  t.score_out = nullptr;
   t.idx = idx;
   t.k = k;
   if (hylra_status st = device_status(hylra::launch_topk(t, shape->batch, hip_stream), "top-k launch"))

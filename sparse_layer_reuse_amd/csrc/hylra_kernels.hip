@@ -5,20 +5,21 @@
 // extraction; reuse layers: attention over the carried KV subset) and 2.4
 // (selection over fixed 128-token blocks).
 //
-// Kernels
-//   attn_split_bf16<D>  split-KV decode attention, bf16 K/V, MFMA
-//                       (v_mfma_f32_16x16x32_bf16) for q.K and p.V; one
-//                       wavefront consumes 32-token chunks, a workgroup of four
-//                       wavefronts merges its partial softmax states in LDS.
-//                       Full mode walks every chunk of a sequence, sparse mode
-//                       the chunks of the selected blocks (through the table).
-//   attn_split_f32<D>   the same contract for float32 K/V on the vector ALU.
-//   merge_heads         per (sequence, query head): merges the split partials
-//                       into out / lse and turns per-chunk statistics into the
-//                       head's probability mass per block.
-//   score_topk          per (sequence, KV head): block score = sum of the
-//                       group's head masses; radix select of the top-k with the
-//                       lower block id winning ties; ascending compaction.
+// One launch per layer.  Grid (nsplit, Hkv, B), 256 threads (4 wavefronts).
+//   split pass   each wavefront consumes 32-token chunks of its workgroup's
+//                range, keeping an online-softmax state for the G query heads
+//                of the KV head; the four states are merged in LDS and written
+//                as the workgroup's partial.  bf16 K/V: q.K and p.V on MFMA
+//                (v_mfma_f32_16x16x32_bf16); float32 K/V: vector ALU.
+//                Full mode walks every chunk of the sequence (and records the
+//                per-chunk softmax mass for block scores); sparse mode walks
+//                the chunks of the selected blocks through the block table.
+//   epilogue     the last workgroup of a (sequence, KV head) to finish (device
+//                scope arrival counter; partials handed over with coherent
+//                device-scope stores and loads) merges them into out / lse and,
+//                in full mode, turns the chunk masses into block scores and
+//                selects the top-k blocks (radix select, lower id wins ties).
+// A separate small kernel selects the top-k of a caller-given score array.
 //
 // Softmax state is kept in base 2: x = s * scale * log2(e), p = 2^(x - m).
 #include <hip/hip_runtime.h>
@@ -33,14 +34,30 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 (raw 32-bit data) on gfx9
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Cross-workgroup hand-off of partials and chunk statistics: relaxed
+// device-scope atomic stores / loads are coherent per location across the
+// XCDs (they bypass stale cache lines), so the hand-off needs no cache-wide
+// release / acquire fence.  Ordering comes from waiting for the stores to
+// complete before the arrival counter is bumped, and from reading only after
+// the counter shows every workgroup has arrived.
+__device__ __forceinline__ void store_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ int clamp_ctx(int t, int max_blocks) {
   return t < 0 ? 0 : (t > max_blocks * kBlockTokens ? max_blocks * kBlockTokens : t);
@@ -54,43 +71,243 @@ __device__ __forceinline__ int chunk_positions(int T, const int32_t *sel, int k)
   return kChunksPerBlock * (k < nb ? k : nb);
 }
 
-// Resolves chunk position `pos` of (b, g) to its page and the valid tokens.
-// Returns false when the chunk holds no token to read (past the context, a
-// padding / out-of-range selected id, or a page outside the pool).
+// Resolves chunk position `pos` of (b, g) to its page and the valid tokens
+// (all arguments wavefront-uniform).  Returns false when the chunk holds no
+// token to read: past the context, a padding / out-of-range selected id, or a
+// page outside the pool.
 __device__ __forceinline__ bool resolve_chunk(const AttnArgs &a, int b, int g, int T, int pos,
-                                              int64_t &page, int &sub, int &valid) {
+                                              int &page, int &sub, int &valid) {
   int n;
   if (a.sel == nullptr) {
     n = pos / kChunksPerBlock;
   } else {
-    n = a.sel[((int64_t)b * a.num_kv_heads + g) * a.k + pos / kChunksPerBlock];
+    n = uniform(a.sel[((int64_t)b * a.num_kv_heads + g) * a.k + pos / kChunksPerBlock]);
     if (n < 0 || n >= (T + kBlockTokens - 1) / kBlockTokens) return false;
   }
   sub = pos % kChunksPerBlock;
   valid = T - (n * kBlockTokens + sub * kChunkTokens);
   if (valid <= 0) return false;
   if (valid > kChunkTokens) valid = kChunkTokens;
-  page = a.table[(int64_t)b * a.max_blocks + n];
+  page = uniform(a.table[(int64_t)b * a.max_blocks + n]);
   return page >= 0 && page < a.num_pages;
 }
 
-__device__ __forceinline__ float wave_max_xor_16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
 }
 
-__device__ __forceinline__ float wave_sum_xor_16_32(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
-// Merges the (m, l, o) states of the four wavefronts of a workgroup (LDS) and
-// writes the workgroup's partial for split `s`.  sm_o is [4][16][D].
+// Exclusive prefix sum over the 256 threads' values.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *tmp) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += tmp[i];
+  return base + inc - v;
+}
+
+// LDS used by the epilogue and the top-k selection.
+struct EpiSmem {
+  float f[kMaxGroup][kMaxSplits];  // per (head, split) rescale factor 2^(m_s - M)
+  float M[kMaxGroup];
+  float L[kMaxGroup];
+  uint32_t keys[kMaxBlocks];
+  int hist[256];
+  int scan[kWaves];
+  int pick_digit;
+  int pick_remaining;
+};
+
+// Selects the k_eff = min(k, N) largest keys[0..N) (unsigned compare), equal
+// keys going to the lower index, and writes their indices in ascending order
+// to out[0..k_eff), -1 after.  keys must be in LDS and visible to all threads.
+// Radix select over 4 x 8 bits finds the k_eff-th largest key `thr`; keys
+// above thr are taken, keys equal to thr in index order until k_eff.
+__device__ void select_topk(EpiSmem &sm, int N, int k, int32_t *out) {
+  const int keff = k < N ? k : N;
+  if (keff == N) {  // every block is selected (also N == 0)
+    for (int r = threadIdx.x; r < k; r += kThreads) out[r] = r < N ? r : -1;
+    return;
+  }
+  uint32_t prefix = 0u, mask = 0u;
+  int remaining = keff;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    __syncthreads();
+    sm.hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int n = threadIdx.x; n < N; n += kThreads)
+      if ((sm.keys[n] & mask) == prefix) atomicAdd(&sm.hist[(sm.keys[n] >> shift) & 255u], 1);
+    __syncthreads();
+    const int rb = 255 - threadIdx.x;  // bins in descending order
+    const int cnt = sm.hist[rb];
+    const int above = block_exclusive_scan(cnt, sm.scan);  // keys in bins > rb
+    if (above < remaining && remaining <= above + cnt) {
+      sm.pick_digit = rb;
+      sm.pick_remaining = remaining - above;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sm.pick_digit << shift;
+    mask |= 255u << shift;
+    remaining = sm.pick_remaining;
+  }
+  const uint32_t thr = prefix;
+  const int need_eq = remaining;
+
+  // contiguous range per thread keeps index order for the scans
+  const int per = (N + kThreads - 1) / kThreads;
+  const int lo = threadIdx.x * per, hi = min(N, lo + per);
+  int eq_cnt = 0;
+  for (int n = lo; n < hi; ++n) eq_cnt += sm.keys[n] == thr;
+  const int eq_rank = block_exclusive_scan(eq_cnt, sm.scan);
+  int sel_cnt = 0;
+  {
+    int r = eq_rank;
+    for (int n = lo; n < hi; ++n) {
+      const uint32_t kv = sm.keys[n];
+      if (kv > thr) {
+        ++sel_cnt;
+      } else if (kv == thr) {
+        if (r < need_eq) ++sel_cnt;
+        ++r;
+      }
+    }
+  }
+  int pos = block_exclusive_scan(sel_cnt, sm.scan);
+  {
+    int r = eq_rank;
+    for (int n = lo; n < hi; ++n) {
+      const uint32_t kv = sm.keys[n];
+      bool take = false;
+      if (kv > thr) {
+        take = true;
+      } else if (kv == thr) {
+        take = r < need_eq;
+        ++r;
+      }
+      if (take) out[pos++] = n;
+    }
+  }
+  for (int r = keff + threadIdx.x; r < k; r += kThreads) out[r] = -1;
+}
+
+// Outputs of a (b, g) with no chunk to attend (empty context).
+__device__ void write_empty(const AttnArgs &a, int b, int g, int D) {
+  const int G = a.group;
+  for (int i = threadIdx.x; i < G * D; i += kThreads)
+    a.out[((int64_t)b * a.num_q_heads + g * G) * D + i] = 0.f;
+  if (a.lse != nullptr)
+    for (int h = threadIdx.x; h < G; h += kThreads)
+      a.lse[(int64_t)b * a.num_q_heads + g * G + h] = kNegInf;
+  if (a.score_out != nullptr)
+    for (int n = threadIdx.x; n < a.max_blocks; n += kThreads)
+      a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = 0.f;
+  if (a.idx_out != nullptr)
+    for (int r = threadIdx.x; r < a.k; r += kThreads)
+      a.idx_out[((int64_t)b * a.num_kv_heads + g) * a.k + r] = -1;
+  if (a.sel_log != nullptr)
+    for (int r = threadIdx.x; r < a.k; r += kThreads) {
+      const int64_t i = ((int64_t)b * a.num_kv_heads + g) * a.k + r;
+      a.sel_log[i] = a.sel[i];
+    }
+}
+
+// Merges the nact split partials of (b, g) into out / lse; in full mode with
+// statistics also the block scores and the top-k.  Runs in the last
+// workgroup of (b, g) to finish its split pass.
 template <int D>
-__device__ __forceinline__ void write_wg_partial(const AttnArgs &a, int b, int g, int s,
-                                                 const float (*sm_m)[kMaxGroup],
-                                                 const float (*sm_l)[kMaxGroup],
-                                                 const float (*sm_o)[kMaxGroup][D]) {
+__device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
+  const int G = a.group;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
+
+  // per head: global max / sum and the per-split rescale factors
+  for (int h = w; h < G; h += kWaves) {
+    const float *ml = a.part_ml + (head0 + h) * a.nsplit * 2;
+    float mx = kNegInf;
+    for (int s = lane; s < nact; s += 64) mx = fmaxf(mx, load_agent(ml + 2 * s));
+    const float M = wave_max(mx);
+    float lsum = 0.f;
+    for (int s = lane; s < nact; s += 64) {
+      const float ms = load_agent(ml + 2 * s);
+      const float f = ms == kNegInf ? 0.f : fast_exp2(ms - M);
+      sm.f[h][s] = f;
+      lsum += f * load_agent(ml + 2 * s + 1);
+    }
+    const float L = wave_sum(lsum);
+    if (lane == 0) {
+      sm.M[h] = M;
+      sm.L[h] = L;
+    }
+  }
+  __syncthreads();
+
+  for (int item = threadIdx.x; item < G * D; item += kThreads) {
+    const int h = item / D, c = item % D;
+    const float *po = a.part_o + (head0 + h) * a.nsplit * D + c;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < nact; ++s) acc += load_agent(po + (int64_t)s * D) * sm.f[h][s];
+    const float L = sm.L[h];
+    a.out[(head0 + h) * D + c] = L > 0.f ? acc / L : 0.f;
+  }
+  if (a.lse != nullptr && threadIdx.x < G) {
+    const float L = sm.L[threadIdx.x];
+    a.lse[head0 + threadIdx.x] = L > 0.f ? (sm.M[threadIdx.x] + __log2f(L)) * kLn2 : kNegInf;
+  }
+
+  if (a.sel_log != nullptr) {
+    const int64_t r0 = ((int64_t)b * a.num_kv_heads + g) * a.k;
+    for (int r = threadIdx.x; r < a.k; r += kThreads) a.sel_log[r0 + r] = a.sel[r0 + r];
+  }
+  if (a.stats == nullptr) return;
+
+  // block score: sum over the group's heads of the softmax mass of the block
+  const int N = (T + kBlockTokens - 1) / kBlockTokens;
+  const int nchunks = (T + kChunkTokens - 1) / kChunkTokens;
+  const int64_t stride = (int64_t)kChunksPerBlock * a.max_blocks * 2;
+  for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
+    float score = 0.f;
+    if (n < N) {
+      for (int h = 0; h < G; ++h) {
+        const float L = sm.L[h];
+        if (!(L > 0.f)) continue;
+        const float *st = a.stats + (head0 + h) * stride;
+        float mass = 0.f;
+        for (int c = n * kChunksPerBlock; c < (n + 1) * kChunksPerBlock && c < nchunks; ++c)
+          mass += load_agent(st + 2 * c + 1) * fast_exp2(load_agent(st + 2 * c) - sm.M[h]);
+        score += mass / L;
+      }
+      sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
+    }
+    if (a.score_out != nullptr)
+      a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = score;
+  }
+  if (a.idx_out != nullptr) {
+    __syncthreads();
+    select_topk(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
+  }
+}
+
+// Writes the workgroup partial from the four wavefront states in LDS, then
+// counts the workgroup's arrival; the last of the nact workgroups of (b, g)
+// runs the epilogue.  Returns true in that workgroup.
+template <int D>
+__device__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact,
+                             const float (*sm_m)[kMaxGroup], const float (*sm_l)[kMaxGroup],
+                             const float (*sm_o)[kMaxGroup][D], int *last_flag) {
   for (int item = threadIdx.x; item < a.group * D; item += kThreads) {
     const int h = item / D, c = item % D;
     float m = kNegInf;
@@ -104,12 +321,27 @@ __device__ __forceinline__ void write_wg_partial(const AttnArgs &a, int b, int g
       l += f * sm_l[w][h];
     }
     const int64_t row = ((int64_t)b * a.num_q_heads + g * a.group + h) * a.nsplit + s;
-    a.part_o[row * D + c] = o;
+    store_agent(a.part_o + row * D + c, o);
     if (c == 0) {
-      a.part_ml[row * 2 + 0] = m;
-      a.part_ml[row * 2 + 1] = l;
+      store_agent(a.part_ml + row * 2 + 0, m);
+      store_agent(a.part_ml + row * 2 + 1, l);
     }
   }
+  // every store of this workgroup (partial and chunk statistics) completes
+  // before the arrival is counted; the last arrival then reads everyone's.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t *cnt = a.counters + (int64_t)b * a.num_kv_heads + g;
+    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == nact - 1;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *last_flag != 0;
+  __syncthreads();  // the epilogue reuses the LDS of the split pass
+  return last;
 }
 
 // ---------------------------------------------------------------------------
@@ -133,33 +365,32 @@ struct BfTile {
 };
 
 template <int D>
-__device__ __forceinline__ void load_bf_tile(BfTile<D> &t, const uint16_t *kbase,
-                                             const uint16_t *vbase, int quad, int m16) {
-  const int tok = 8 * (m16 >> 2) + (m16 & 3);
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      t.k[a][s] = *reinterpret_cast<const u32x4 *>(kbase + (tok + 4 * a) * D + 32 * s + 8 * quad);
-#pragma unroll
-  for (int n = 0; n < D / 16; ++n)
-    t.v[n] = *reinterpret_cast<const u32x4 *>(vbase + (16 * n + m16) * kBlockTokens + 8 * quad);
-}
+union BfSmem {
+  struct {
+    float m[kWaves][kMaxGroup];
+    float l[kWaves][kMaxGroup];
+    float o[kWaves][kMaxGroup][D];
+  } main;
+  EpiSmem epi;
+};
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_split_bf16(AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int T = clamp_ctx(a.ctx[b], a.max_blocks);
   const int C = chunk_positions(T, a.sel, a.k);
+  __shared__ BfSmem<D> sm;
+  __shared__ int last_flag;
+  if (C == 0) {
+    if (s == 0) write_empty(a, b, g, D);
+    return;
+  }
   const int c_begin = s * a.chunks_per_wg;
   if (c_begin >= C) return;
   const int c_end = min(C, c_begin + a.chunks_per_wg);
+  const int nact = (C + a.chunks_per_wg - 1) / a.chunks_per_wg;
 
-  __shared__ float sm_m[kWaves][kMaxGroup];
-  __shared__ float sm_l[kWaves][kMaxGroup];
-  __shared__ float sm_o[kWaves][kMaxGroup][D];
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int quad = lane >> 4, m16 = lane & 15;
   const int G = a.group;
 
@@ -180,27 +411,53 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
 #pragma unroll
   for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t *kpool = static_cast<const uint16_t *>(a.k_pool);
-  const uint16_t *vpool = static_cast<const uint16_t *>(a.v_pool);
+  const char *kpool = static_cast<const char *>(a.k_pool);
+  const char *vpool = static_cast<const char *>(a.v_pool);
   const int Hkv = a.num_kv_heads;
+  // per-lane byte offsets inside a chunk's K rows / V columns (chunk-invariant)
+  const uint32_t k_lane = (uint32_t)(((8 * (m16 >> 2) + (m16 & 3)) * D + 8 * quad) * 2);
+  const uint32_t v_lane = (uint32_t)((m16 * kBlockTokens + 8 * quad) * 2);
   float *stats_row = a.stats ? a.stats + ((int64_t)b * a.num_q_heads + g * G + m16) *
                                              (int64_t)(kChunksPerBlock * a.max_blocks) * 2
                              : nullptr;
 
-  auto issue = [&](BfTile<D> &t, int pos, int &valid) -> bool {
-    int64_t page;
-    int sub;
-    if (!resolve_chunk(a, b, g, T, pos, page, sub, valid)) {
-      if (stats_row != nullptr && quad == 0 && m16 < G) {  // unreadable page: no mass
-        stats_row[2 * pos + 0] = kNegInf;
-        stats_row[2 * pos + 1] = 0.f;
+  // Issues the 16-byte loads of chunk `pos` into t through buffer resources
+  // spanning just that chunk; returns its valid token count.  A position past
+  // the range or without a readable page gets an empty resource: the loads
+  // return zeros without touching memory, so every path issues the same loads
+  // and the register tiles never need copying.
+  auto issue = [&](BfTile<D> &t, int pos) -> int {
+    int page = 0, sub = 0, valid = 0;
+    bool ok = false;
+    if (pos < c_end) {
+      ok = resolve_chunk(a, b, g, T, pos, page, sub, valid);
+      if (!ok && stats_row != nullptr && quad == 0 && m16 < G) {  // unreadable page: no mass
+        store_agent(stats_row + 2 * pos + 0, kNegInf);
+        store_agent(stats_row + 2 * pos + 1, 0.f);
       }
-      return false;
     }
-    const int64_t tile = page * Hkv + g;
-    load_bf_tile<D>(t, kpool + (tile * kBlockTokens + sub * kChunkTokens) * D,
-                    vpool + tile * D * kBlockTokens + sub * kChunkTokens, quad, m16);
-    return true;
+    if (!ok) {
+      page = 0;
+      sub = 0;
+      valid = 0;
+    }
+    const int64_t tile = (int64_t)page * Hkv + g;
+    const char *kb = kpool + (tile * kBlockTokens + sub * kChunkTokens) * D * 2;
+    const char *vb = vpool + (tile * D * kBlockTokens + sub * kChunkTokens) * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(kb), (short)0, ok ? kChunkTokens * D * 2 : 0, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(vb), (short)0, ok ? (D - 1) * kBlockTokens * 2 + kChunkTokens * 2 : 0,
+        kBufferFlags);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int k = 0; k < D / 32; ++k)
+        t.k[h][k] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane, (4 * h * D + 32 * k) * 2, 0);
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+      t.v[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_lane, n * 16 * kBlockTokens * 2, 0);
+    return valid;
   };
 
   auto consume = [&](const BfTile<D> &t, int pos, int valid) {
@@ -222,49 +479,44 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
       x[j] = tok < valid ? sacc[j >> 2][j & 3] * a.scale_log2 : kNegInf;
       mx = fmaxf(mx, x[j]);
     }
-    mx = wave_max_xor_16_32(mx);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float alpha = fast_exp2(m_run - m_new);
-    float p[8];
     float ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = fast_exp2(x[j] - m_new);
-      ps += p[j];
-    }
-    ps = wave_sum_xor_16_32(ps);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    if (stats_row != nullptr && quad == 0 && m16 < G) {
-      stats_row[2 * pos + 0] = m_new;
-      stats_row[2 * pos + 1] = ps;
-    }
     bf16x8 phi, plo;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const __bf16 hi = (__bf16)p[j];
+      const float p = fast_exp2(x[j] - m_new);
+      ps += p;
+      const __bf16 hi = (__bf16)p;
       phi[j] = hi;
-      plo[j] = (__bf16)(p[j] - (float)hi);
+      plo[j] = (__bf16)(p - (float)hi);
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (stats_row != nullptr && quad == 0 && m16 < G) {
+      store_agent(stats_row + 2 * pos + 0, m_new);
+      store_agent(stats_row + 2 * pos + 1, ps);
     }
     float al[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * quad + r);
+    // tokens past the context: p is 0 there, and V is zeroed so stale page
+    // bytes (possibly NaN patterns) cannot leak in through 0 * NaN.
+    u32x4 keep;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = 8 * quad + 2 * e;
+      keep[e] = (tok < valid ? 0x0000FFFFu : 0u) | (tok + 1 < valid ? 0xFFFF0000u : 0u);
+    }
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[n][r] *= al[r];
-      u32x4 v = t.v[n];
-      if (valid < kChunkTokens) {
-        // tokens past the context: p is 0 there, zero V so stale page bytes
-        // (possibly NaN patterns) cannot leak in through 0 * NaN.
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = 8 * quad + 2 * e;
-          uint32_t keep = (tok < valid ? 0x0000FFFFu : 0u) | (tok + 1 < valid ? 0xFFFF0000u : 0u);
-          v[e] &= keep;
-        }
-      }
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, v);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, t.v[n] & keep);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, acc[n], 0, 0, 0);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, acc[n], 0, 0, 0);
     }
@@ -274,30 +526,28 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
   // current one is consumed.
   BfTile<D> ta, tb;
   int pos = c_begin + w;
-  int va = 0, vb = 0;
-  bool ha = pos < c_end ? issue(ta, pos, va) : false;
+  int va = issue(ta, pos);
   while (pos < c_end) {
-    const int pn = pos + kWaves;
-    bool hb = pn < c_end ? issue(tb, pn, vb) : false;
-    if (ha) consume(ta, pos, va);
-    pos = pn;
+    const int vb = issue(tb, pos + kWaves);
+    if (va > 0) consume(ta, pos, va);
+    pos += kWaves;
     if (pos >= c_end) break;
-    const int pn2 = pos + kWaves;
-    ha = pn2 < c_end ? issue(ta, pn2, va) : false;
-    if (hb) consume(tb, pos, vb);
-    pos = pn2;
+    va = issue(ta, pos + kWaves);
+    if (vb > 0) consume(tb, pos, vb);
+    pos += kWaves;
   }
 
   if (quad == 0) {
-    sm_m[w][m16] = m_run;
-    sm_l[w][m16] = l_run;
+    sm.main.m[w][m16] = m_run;
+    sm.main.l[w][m16] = l_run;
   }
 #pragma unroll
   for (int n = 0; n < D / 16; ++n)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm_o[w][4 * quad + r][16 * n + m16] = acc[n][r];
+    for (int r = 0; r < 4; ++r) sm.main.o[w][4 * quad + r][16 * n + m16] = acc[n][r];
   __syncthreads();
-  write_wg_partial<D>(a, b, g, s, sm_m, sm_l, sm_o);
+  if (!finish_split<D>(a, b, g, s, nact, sm.main.m, sm.main.l, sm.main.o, &last_flag)) return;
+  epilogue<D>(a, b, g, T, nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -306,26 +556,39 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
 // group; p.V runs with lane i owning columns i and i+64.
 // ---------------------------------------------------------------------------
 template <int D>
+union F32Smem {
+  struct {
+    float q[kMaxGroup][D];
+    float m[kWaves][kMaxGroup];
+    float l[kWaves][kMaxGroup];
+    float o[kWaves][kMaxGroup][D];
+  } main;
+  EpiSmem epi;
+};
+
+template <int D>
 __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int T = clamp_ctx(a.ctx[b], a.max_blocks);
   const int C = chunk_positions(T, a.sel, a.k);
+  __shared__ F32Smem<D> sm;
+  __shared__ int last_flag;
+  if (C == 0) {
+    if (s == 0) write_empty(a, b, g, D);
+    return;
+  }
   const int c_begin = s * a.chunks_per_wg;
   if (c_begin >= C) return;
   const int c_end = min(C, c_begin + a.chunks_per_wg);
+  const int nact = (C + a.chunks_per_wg - 1) / a.chunks_per_wg;
 
   constexpr int CPL = D / 64;  // output columns per lane
-  __shared__ float q_s[kMaxGroup][D];
-  __shared__ float sm_m[kWaves][kMaxGroup];
-  __shared__ float sm_l[kWaves][kMaxGroup];
-  __shared__ float sm_o[kWaves][kMaxGroup][D];
-
   const int G = a.group;
   const float *qg = static_cast<const float *>(a.q) + ((int64_t)b * a.num_q_heads + g * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) q_s[i / D][i % D] = qg[i];
+  for (int i = threadIdx.x; i < G * D; i += kThreads) sm.main.q[i / D][i % D] = qg[i];
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int t = lane & 31, half = lane >> 5;
   const float *kpool = static_cast<const float *>(a.k_pool);
   const float *vpool = static_cast<const float *>(a.v_pool);
@@ -341,18 +604,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   }
 
   for (int pos = c_begin + w; pos < c_end; pos += kWaves) {
-    int64_t page;
-    int sub, valid;
+    int page, sub, valid;
     if (!resolve_chunk(a, b, g, T, pos, page, sub, valid)) {
       if (a.stats != nullptr && lane < G) {  // unreadable page: no mass
         float *st = a.stats + ((int64_t)b * a.num_q_heads + g * G + lane) *
                                   (int64_t)(kChunksPerBlock * a.max_blocks) * 2;
-        st[2 * pos + 0] = kNegInf;
-        st[2 * pos + 1] = 0.f;
+        store_agent(st + 2 * pos + 0, kNegInf);
+        store_agent(st + 2 * pos + 1, 0.f);
       }
       continue;
     }
-    const int64_t tile = page * Hkv + g;
+    const int64_t tile = (int64_t)page * Hkv + g;
     const float *krow = kpool + (tile * kBlockTokens + sub * kChunkTokens + t) * D + half * (D / 2);
     float sc[kMaxGroup];
 #pragma unroll
@@ -363,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h) {
           if (h < G) {
-            const float *qh = &q_s[h][half * (D / 2) + c];
+            const float *qh = &sm.main.q[h][half * (D / 2) + c];
             sc[h] += qh[0] * kv.x + qh[1] * kv.y + qh[2] * kv.z + qh[3] * kv.w;
           }
         }
@@ -389,8 +651,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
       if (a.stats != nullptr && lane == 0) {
         float *st = a.stats + ((int64_t)b * a.num_q_heads + g * G + h) *
                                   (int64_t)(kChunksPerBlock * a.max_blocks) * 2;
-        st[2 * pos + 0] = m_new;
-        st[2 * pos + 1] = ps;
+        store_agent(st + 2 * pos + 0, m_new);
+        store_agent(st + 2 * pos + 1, ps);
       }
     }
 #pragma unroll
@@ -413,212 +675,38 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
     }
   }
 
+  __syncthreads();  // q no longer read; the merge arrays follow it in LDS
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h >= G) continue;
     if (lane == 0) {
-      sm_m[w][h] = m_run[h];
-      sm_l[w][h] = l_run[h];
+      sm.main.m[w][h] = m_run[h];
+      sm.main.l[w][h] = l_run[h];
     }
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) sm_o[w][h][lane + 64 * j] = acc[h][j];
+    for (int j = 0; j < CPL; ++j) sm.main.o[w][h][lane + 64 * j] = acc[h][j];
   }
   __syncthreads();
-  write_wg_partial<D>(a, b, g, s, sm_m, sm_l, sm_o);
+  if (!finish_split<D>(a, b, g, s, nact, sm.main.m, sm.main.l, sm.main.o, &last_flag)) return;
+  epilogue<D>(a, b, g, T, nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
-// Block reductions / scans for 256-thread workgroups.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_max(float v, float *red) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-__device__ __forceinline__ float block_sum(float v, float *red) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-// Exclusive prefix sum over the 256 threads' values; also returns the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *tmp, int &total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  __syncthreads();
-  if (lane == 63) tmp[w] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int i = 0; i < w; ++i) base += tmp[i];
-  total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
-  return base + inc - v;
-}
-
-// ---------------------------------------------------------------------------
-// merge_heads: grid (Hq, B).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void merge_heads(MergeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int G = a.group, g = h / G;
-  const int D = a.head_dim;
-  const int T = clamp_ctx(a.ctx[b], a.max_blocks);
-  const int C = chunk_positions(T, a.sel, a.k);
-  const int nact = (C + a.chunks_per_wg - 1) / a.chunks_per_wg;
-  const int64_t row0 = ((int64_t)b * a.num_q_heads + h) * a.nsplit;
-
-  __shared__ float red[kWaves];
-  __shared__ float ocomb[kThreads];
-
-  float mloc = kNegInf;
-  for (int s = threadIdx.x; s < nact; s += kThreads) mloc = fmaxf(mloc, a.part_ml[(row0 + s) * 2]);
-  const float M = block_max(mloc, red);
-  float lloc = 0.f;
-  if (M != kNegInf)
-    for (int s = threadIdx.x; s < nact; s += kThreads) {
-      const float ms = a.part_ml[(row0 + s) * 2];
-      if (ms != kNegInf) lloc += a.part_ml[(row0 + s) * 2 + 1] * fast_exp2(ms - M);
-    }
-  const float L = block_sum(lloc, red);
-
-  // out: thread -> (column c, stripe of splits); stripes combined in LDS
-  const int stripes = kThreads / D;
-  const int c = threadIdx.x % D, stripe = threadIdx.x / D;
-  float o = 0.f;
-  if (L > 0.f)
-    for (int s = stripe; s < nact; s += stripes) {
-      const float ms = a.part_ml[(row0 + s) * 2];
-      if (ms != kNegInf) o += a.part_o[(row0 + s) * D + c] * fast_exp2(ms - M);
-    }
-  ocomb[threadIdx.x] = o;
-  __syncthreads();
-  if (threadIdx.x < D) {
-    float tot = 0.f;
-    for (int st = 0; st < stripes; ++st) tot += ocomb[st * D + threadIdx.x];
-    a.out[((int64_t)b * a.num_q_heads + h) * D + threadIdx.x] = L > 0.f ? tot / L : 0.f;
-  }
-  if (threadIdx.x == 0 && a.lse != nullptr)
-    a.lse[(int64_t)b * a.num_q_heads + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
-
-  if (a.head_mass != nullptr) {
-    const int nb = (T + kBlockTokens - 1) / kBlockTokens;
-    const int nchunks = (T + kChunkTokens - 1) / kChunkTokens;
-    const float *st = a.stats + ((int64_t)b * a.num_q_heads + h) *
-                                    (int64_t)(kChunksPerBlock * a.max_blocks) * 2;
-    float *hm = a.head_mass + ((int64_t)b * a.num_q_heads + h) * a.max_blocks;
-    const float inv_l = L > 0.f ? 1.f / L : 0.f;
-    for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
-      float mass = 0.f;
-      if (n < nb && L > 0.f) {
-        for (int cc = n * kChunksPerBlock; cc < (n + 1) * kChunksPerBlock && cc < nchunks; ++cc)
-          mass += st[2 * cc + 1] * fast_exp2(st[2 * cc] - M);
-        mass *= inv_l;
-      }
-      hm[n] = mass;
-    }
-  }
-  if (a.sel_log != nullptr && h % G == 0) {
-    const int64_t r0 = ((int64_t)b * a.num_kv_heads + g) * a.k;
-    for (int r = threadIdx.x; r < a.k; r += kThreads) a.sel_log[r0 + r] = a.sel[r0 + r];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// score_topk: grid (Hkv, B).  Keys are the float bits of the non-negative
-// block scores (monotone as unsigned integers).  Radix select (4 x 8 bits)
-// finds the k_eff-th largest key; keys above it are taken, keys equal to it
-// are taken in ascending block order until k_eff are chosen.
+// Top-k of a caller-given score array: grid (Hkv, B).  Keys are the float bits
+// of the non-negative scores (monotone as unsigned integers).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void score_topk(TopkArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int T = clamp_ctx(a.ctx[b], a.max_blocks);
   const int N = (T + kBlockTokens - 1) / kBlockTokens;
-
-  __shared__ uint32_t keys[kMaxBlocks];
-  __shared__ int hist[256];
-  __shared__ int scan_tmp[kWaves];
-  __shared__ int pick_digit, pick_remaining;
-
-  const float *base = a.mass + ((int64_t)b * a.num_kv_heads + g) * a.heads_per_row * a.max_blocks;
-  for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
-    float sc = 0.f;
-    if (n < N)
-      for (int h = 0; h < a.heads_per_row; ++h) sc += base[(int64_t)h * a.max_blocks + n];
-    if (a.score_out != nullptr) a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = sc;
-    if (n < N) keys[n] = sc > 0.f ? __float_as_uint(sc) : 0u;
-  }
-  if (a.idx == nullptr) return;
-  int32_t *out = a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k;
-  const int keff = a.k < N ? a.k : N;
-  if (keff == N) {  // every block is selected (also N == 0)
-    for (int r = threadIdx.x; r < a.k; r += kThreads) out[r] = r < N ? r : -1;
-    return;
+  __shared__ EpiSmem sm;
+  const float *row = a.score + ((int64_t)b * a.num_kv_heads + g) * a.max_blocks;
+  for (int n = threadIdx.x; n < N; n += kThreads) {
+    const float sc = row[n];
+    sm.keys[n] = sc > 0.f ? __float_as_uint(sc) : 0u;
   }
   __syncthreads();
-
-  uint32_t prefix = 0u, mask = 0u;
-  int remaining = keff;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int n = threadIdx.x; n < N; n += kThreads)
-      if ((keys[n] & mask) == prefix) atomicAdd(&hist[(keys[n] >> shift) & 255u], 1);
-    __syncthreads();
-    // suffix count of bins >= my bin: scan over reversed bin order
-    const int rb = 255 - threadIdx.x;
-    const int cnt = hist[rb];
-    int total;
-    const int above = block_exclusive_scan(cnt, scan_tmp, total);  // bins > rb
-    if (above < remaining && remaining <= above + cnt) {
-      pick_digit = rb;
-      pick_remaining = remaining - above;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)pick_digit << shift;
-    mask |= 255u << shift;
-    remaining = pick_remaining;
-    __syncthreads();
-  }
-  const uint32_t thr = prefix;
-  const int need_eq = remaining;
-
-  // contiguous element range per thread keeps index order for the scans
-  const int per = (N + kThreads - 1) / kThreads;
-  const int lo = threadIdx.x * per, hi = min(N, lo + per);
-  int eq_cnt = 0;
-  for (int n = lo; n < hi; ++n) eq_cnt += keys[n] == thr;
-  int tot;
-  int eq_rank = block_exclusive_scan(eq_cnt, scan_tmp, tot);
-  int sel_cnt = 0;
-  {
-    int r = eq_rank;
-    for (int n = lo; n < hi; ++n) {
-      const uint32_t kv = keys[n];
-      if (kv > thr) ++sel_cnt;
-      else if (kv == thr) { if (r < need_eq) ++sel_cnt; ++r; }
-    }
-  }
-  int pos = block_exclusive_scan(sel_cnt, scan_tmp, tot);
-  {
-    int r = eq_rank;
-    for (int n = lo; n < hi; ++n) {
-      const uint32_t kv = keys[n];
-      bool take = false;
-      if (kv > thr) take = true;
-      else if (kv == thr) { take = r < need_eq; ++r; }
-      if (take) out[pos++] = n;
-    }
-  }
-  for (int r = keff + threadIdx.x; r < a.k; r += kThreads) out[r] = -1;
+  select_topk(sm, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k);
 }
 
 // Kernel timers: event pairs recorded around launches while running.
@@ -693,13 +781,6 @@ int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *str
     if (head_dim == 128) hipLaunchKernelGGL(attn_split_f32<128>, grid, dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL(attn_split_f32<64>, grid, dim3(kThreads), 0, st, a);
   }
-  return (int)hipGetLastError();
-}
-
-int launch_merge(const MergeArgs &a, int batch, void *stream) {
-  TimerScope timer(kTimerMerge, static_cast<hipStream_t>(stream));
-  hipLaunchKernelGGL(merge_heads, dim3(a.num_q_heads, batch), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhylra.so")
+LIB_PATH = os.environ.get("HYLRA_LIBRARY") or os.path.join(_HERE, "libhylra.so")
 
 OK, E_INVALID_ARG, E_UNSUPPORTED, E_BAD_POLICY, E_WORKSPACE, E_DEVICE = range(6)
 F32, BF16 = 0, 1
@@ -77,9 +77,9 @@ EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
             "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_timer_start",
             "hylra_timer_stop", "hylra_status_str", "hylra_last_error")
 
-KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_MERGE, KERNEL_TOPK = range(4)
-KERNEL_NAMES = {KERNEL_FULL_ATTN: "attn_split_full", KERNEL_SPARSE_ATTN: "attn_split_sparse",
-                KERNEL_MERGE: "merge_heads", KERNEL_TOPK: "score_topk"}
+KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_TOPK = range(3)
+KERNEL_NAMES = {KERNEL_FULL_ATTN: "attn_full_layer", KERNEL_SPARSE_ATTN: "attn_sparse_layer",
+                KERNEL_TOPK: "score_topk"}
 
 
 def _status_str(st: int) -> str:
@@ -154,13 +154,14 @@ _ws_cache = {}
 
 
 def workspace(shape: Shape, k: int, device) -> torch.Tensor:
-    """A cached device workspace big enough for `shape` and `k` (one per device)."""
+    """A cached, zero-initialised device workspace big enough for `shape` and
+    `k` (one per device; calls that share it must run on one stream)."""
     need = workspace_size(shape, k)
     dev = torch.device(device)
     key = (dev.type, dev.index)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 
@@ -250,7 +251,8 @@ class PolicyPlan:
         return self.out, self.lse
 
 
-def run_policy(layers, src, k, *, scale=0.0, idx_log=None, ws=None, stream=None):
+def run_policy(layers, src, k, *, scale=0.0, idx_log=None, outs=None, lses=None, ws=None,
+               stream=None):
     """One hybrid decode step over the layers (list of dicts with q, k_pool,
     v_pool, table, ctx).  Returns (outs, lses, idx_log)."""
     if idx_log is None:
@@ -258,7 +260,7 @@ def run_policy(layers, src, k, *, scale=0.0, idx_log=None, ws=None, stream=None)
         B = first["q"].shape[0]
         idx_log = torch.full((len(layers), B, first["k_pool"].shape[1], int(k)), -2,
                              dtype=torch.int32, device=first["q"].device)
-    plan = PolicyPlan(layers, src, k, scale=scale, idx_log=idx_log, ws=ws)
+    plan = PolicyPlan(layers, src, k, scale=scale, outs=outs, lses=lses, idx_log=idx_log, ws=ws)
     outs, lses = plan.run(stream)
     return outs, lses, idx_log
 

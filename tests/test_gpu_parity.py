@@ -40,6 +40,20 @@ def gpu_layer(dtype, ctx, Hq, Hkv, d, seed, paged=True, hot=None, alpha=1.5, max
                             alpha=alpha, device="cuda", max_blocks=max_blocks)
 
 
+def nan_out(q):
+    """Output buffers pre-filled with NaN, so a launch that skips a write fails."""
+    B, Hq, d = q.shape
+    return (torch.full((B, Hq, d), float("nan"), device=q.device),
+            torch.full((B, Hq), float("nan"), device=q.device))
+
+
+def counters_are_zero(H, q, k_pool, table, k=0):
+    """The workspace's arrival counters are back at zero after the launches."""
+    torch.cuda.synchronize()
+    ws = H.workspace(H.make_shape(q, k_pool, table), k, q.device)
+    return bool((ws[:65536 * 4].view(torch.int32) == 0).all().item())
+
+
 def assert_close(got, want, tol, what):
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
@@ -69,9 +83,10 @@ def test_decode_full_parity(H, case):
     dtype, ctx, Hq, Hkv, d = case
     say("decode_full", case)
     lay = gpu_layer(dtype, ctx, Hq, Hkv, d, seed=17)
+    o0, l0 = nan_out(lay["q"])
     out, lse, score = H.decode_full(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"],
-                                    lay["ctx"], want_scores=True)
-    torch.cuda.synchronize()
+                                    lay["ctx"], want_scores=True, out=o0, lse=l0)
+    assert counters_are_zero(H, lay["q"], lay["k_pool"], lay["table"])
     o = synth.layer_to_oracle(lay)
     r_out, r_lse, r_score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
                                                o["ctx"], num_kv_heads=Hkv)
@@ -166,9 +181,10 @@ def test_decode_sparse_parity(H, case):
     say("decode_sparse", case)
     lay = gpu_layer(dtype, ctx, Hq, Hkv, d, seed=29)
     sel = _random_sel(ctx, Hkv, k, np.random.default_rng(k))
+    o0, l0 = nan_out(lay["q"])
     out, lse = H.decode_sparse(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
-                               torch.from_numpy(sel).cuda())
-    torch.cuda.synchronize()
+                               torch.from_numpy(sel).cuda(), out=o0, lse=l0)
+    assert counters_are_zero(H, lay["q"], lay["k_pool"], lay["table"], k)
     o = synth.layer_to_oracle(lay)
     r_out, r_lse, _ = oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
                                     num_kv_heads=Hkv, sel=sel, k=k)
@@ -195,8 +211,11 @@ def test_decode_sparse_all_blocks_equals_full(H):
 
 def check_policy_run(H, layers_gpu, src, k, dtype, num_kv_heads, check_layers=None):
     """Run the GPU policy and compare the chosen layers with the oracle."""
-    outs, lses, idx_log = H.run_policy(layers_gpu, src, k)
-    torch.cuda.synchronize()
+    bufs = [nan_out(l["q"]) for l in layers_gpu]
+    outs, lses, idx_log = H.run_policy(layers_gpu, src, k, outs=[b[0] for b in bufs],
+                                       lses=[b[1] for b in bufs])
+    first = layers_gpu[0]
+    assert counters_are_zero(H, first["q"], first["k_pool"], first["table"], k)
     idx_gpu = idx_log.cpu().numpy()
     tol = TOL[dtype]
     L = len(layers_gpu)
