@@ -121,7 +121,7 @@ Workspace layout(const hylra_shape *s, int k, void *base) {
   w.counters = reinterpret_cast<int32_t *>(take(hylra::kCounterSlots * sizeof(int32_t)));
   w.part_ml = reinterpret_cast<float *>(take(B * Hq * ns * 2 * sizeof(float)));
   w.part_o = reinterpret_cast<float *>(take(B * Hq * ns * D * sizeof(float)));
-  w.stats = reinterpret_cast<float *>(take(B * Hq * mb * hylra::kChunksPerBlock * 2 * sizeof(float)));
+  w.stats = reinterpret_cast<float *>(take(B * Hq * mb * sizeof(float)));
   w.idx = reinterpret_cast<int32_t *>(take(B * Hkv * (size_t)(k > 0 ? k : 1) * sizeof(int32_t)));
   w.bytes = off;
   return w;
@@ -211,6 +211,9 @@ static SplitPlan make_plan(long chunks_per_seq, long rows) {
   if (cpw < min_cpw) cpw = min_cpw;
   cpw = (cpw + 3) / 4 * 4;
   if (cpw < 4) cpw = 4;
+  // longer ranges would outgrow the per-workgroup block statistics in LDS;
+  // min_cpw <= 128 always (at most 4 * kMaxBlocks chunks over kMaxSplits)
+  if (cpw > kMaxWgChunks) cpw = kMaxWgChunks;
   SplitPlan p;
   p.chunks_per_wg = (int)cpw;
   p.nsplit = (int)((chunks_per_seq + cpw - 1) / cpw);

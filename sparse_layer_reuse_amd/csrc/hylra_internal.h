@@ -13,6 +13,7 @@ constexpr int kMaxGroup = 16;      // query heads per KV head handled by one til
 constexpr int kMaxBlocks = 8192;   // blocks per sequence (1M tokens)
 constexpr int kMaxSplits = 256;    // workgroups per (sequence, KV head)
 constexpr int kCounterSlots = 65536;  // (sequence, KV head) arrival counters in a workspace
+constexpr int kMaxWgChunks = 256;     // chunk positions per workgroup (64 blocks)
 
 // Work split of one attention launch: each workgroup (4 wavefronts) takes
 // `chunks_per_wg` consecutive 32-token chunk positions of one (sequence, KV
@@ -45,7 +46,8 @@ struct AttnArgs {
   // workspace
   float *part_ml;      // [B][Hq][nsplit][2]  running max (log2 units) and sum
   float *part_o;       // [B][Hq][nsplit][d]  unnormalised output
-  float *stats;        // full mode with scores: [B][Hq][4*max_blocks][2] per chunk (max, mass)
+  float *stats;        // full mode with scores: [B][Hq][max_blocks] block mass, relative to
+                       // the running max of the block's workgroup partial
   int32_t *counters;   // [B][Hkv] arrival counters, zero between launches
   // outputs
   float *out;          // [B][Hq][d]

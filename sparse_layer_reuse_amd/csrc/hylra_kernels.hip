@@ -11,13 +11,14 @@
 //                of the KV head; the four states are merged in LDS and written
 //                as the workgroup's partial.  bf16 K/V: q.K and p.V on MFMA
 //                (v_mfma_f32_16x16x32_bf16); float32 K/V: vector ALU.
-//                Full mode walks every chunk of the sequence (and records the
-//                per-chunk softmax mass for block scores); sparse mode walks
-//                the chunks of the selected blocks through the block table.
+//                Full mode walks every chunk of the sequence, a wavefront
+//                taking whole 128-token blocks so it can also sum each block's
+//                softmax mass; sparse mode walks the chunks of the selected
+//                blocks through the block table.
 //   epilogue     the last workgroup of a (sequence, KV head) to finish (device
 //                scope arrival counter; partials handed over with coherent
 //                device-scope stores and loads) merges them into out / lse and,
-//                in full mode, turns the chunk masses into block scores and
+//                in full mode, turns the block masses into block scores and
 //                selects the top-k blocks (radix select, lower id wins ties).
 // A separate small kernel selects the top-k of a caller-given score array.
 //
@@ -38,25 +39,43 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
+constexpr int kMaxWgBlocks = kMaxWgChunks / kChunksPerBlock;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 (raw 32-bit data) on gfx9
+constexpr int kCoherent = 16;             // buffer instruction cache policy: sc1
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^(m - ref) for a state with running max m (-inf: empty state -> 0).
+__device__ __forceinline__ float rescale(float m, float ref) {
+  return m == kNegInf ? 0.f : fast_exp2(m - ref);
+}
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Cross-workgroup hand-off of partials and chunk statistics: relaxed
-// device-scope atomic stores / loads are coherent per location across the
-// XCDs (they bypass stale cache lines), so the hand-off needs no cache-wide
-// release / acquire fence.  Ordering comes from waiting for the stores to
-// complete before the arrival counter is bumped, and from reading only after
-// the counter shows every workgroup has arrived.
+// Wavefront-uniform read of a read-only int array through the scalar cache
+// (constant address space): an s_load, counted apart from the vector loads,
+// so it never waits for the K/V tiles in flight.
+typedef const __attribute__((address_space(4))) int32_t *ConstI32Ptr;
+__device__ __forceinline__ int scalar_load(const int32_t *p, int64_t i) {
+  return ((ConstI32Ptr)(p))[i];
+}
+
+// Cross-workgroup hand-off of partials and block masses: device-scope
+// coherent (sc1) stores and loads act per location across the XCDs without a
+// cache-wide release / acquire fence.  Ordering comes from waiting for the
+// stores to complete before the arrival counter is bumped, and from reading
+// only after the counter shows that every workgroup has arrived.
 __device__ __forceinline__ void store_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float load_agent(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kBufferFlags);
 }
 
 __device__ __forceinline__ int clamp_ctx(int t, int max_blocks) {
@@ -81,15 +100,30 @@ __device__ __forceinline__ bool resolve_chunk(const AttnArgs &a, int b, int g, i
   if (a.sel == nullptr) {
     n = pos / kChunksPerBlock;
   } else {
-    n = uniform(a.sel[((int64_t)b * a.num_kv_heads + g) * a.k + pos / kChunksPerBlock]);
+    n = scalar_load(a.sel, ((int64_t)b * a.num_kv_heads + g) * a.k + pos / kChunksPerBlock);
     if (n < 0 || n >= (T + kBlockTokens - 1) / kBlockTokens) return false;
   }
   sub = pos % kChunksPerBlock;
   valid = T - (n * kBlockTokens + sub * kChunkTokens);
   if (valid <= 0) return false;
   if (valid > kChunkTokens) valid = kChunkTokens;
-  page = uniform(a.table[(int64_t)b * a.max_blocks + n]);
+  page = scalar_load(a.table, (int64_t)b * a.max_blocks + n);
   return page >= 0 && page < a.num_pages;
+}
+
+// The i-th chunk position of wavefront w in a workgroup range starting at
+// c_begin.  Full mode (blocked): wavefront w takes whole blocks w, w+4, ...
+// Sparse mode: chunks are dealt round-robin.
+__device__ __forceinline__ int chunk_of(bool blocked, int c_begin, int w, int i) {
+  return blocked ? c_begin + kChunksPerBlock * (w + kWaves * (i / kChunksPerBlock)) +
+                       i % kChunksPerBlock
+                 : c_begin + w + kWaves * i;
+}
+// Whether the i-th chunk of wavefront w still belongs to the range (for the
+// blocked order: whether its block starts inside the range).
+__device__ __forceinline__ bool chunk_live(bool blocked, int c_begin, int c_end, int w, int i) {
+  return blocked ? c_begin + kChunksPerBlock * (w + kWaves * (i / kChunksPerBlock)) < c_end
+                 : c_begin + w + kWaves * i < c_end;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -118,16 +152,33 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *tmp) {
   return base + inc - v;
 }
 
+// LDS of the split pass: the four wavefront states and the block masses.
+template <int D>
+struct SplitSmem {
+  float m[kWaves][kMaxGroup];
+  float l[kWaves][kMaxGroup];
+  float o[kWaves][kMaxGroup][D];
+  float bm[kMaxWgBlocks][kMaxGroup];  // block: running max when its mass was taken
+  float bp[kMaxWgBlocks][kMaxGroup];  // block: softmax mass relative to bm
+};
+
 // LDS used by the epilogue and the top-k selection.
 struct EpiSmem {
   float f[kMaxGroup][kMaxSplits];  // per (head, split) rescale factor 2^(m_s - M)
   float M[kMaxGroup];
   float L[kMaxGroup];
+  f32x4 red[kThreads];
   uint32_t keys[kMaxBlocks];
   int hist[256];
   int scan[kWaves];
   int pick_digit;
   int pick_remaining;
+};
+
+template <int D>
+union KernelSmem {
+  SplitSmem<D> split;
+  EpiSmem epi;
 };
 
 // Selects the k_eff = min(k, N) largest keys[0..N) (unsigned compare), equal
@@ -224,111 +275,54 @@ __device__ void write_empty(const AttnArgs &a, int b, int g, int D) {
     }
 }
 
-// Merges the nact split partials of (b, g) into out / lse; in full mode with
-// statistics also the block scores and the top-k.  Runs in the last
-// workgroup of (b, g) to finish its split pass.
+// Writes the workgroup partial from the four wavefront states (and, in full
+// mode with scores, the block masses rescaled to the partial's max), then
+// counts the workgroup's arrival.  Returns true in the last of the nact
+// workgroups of (b, g), which then runs the epilogue.
 template <int D>
-__device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
+__device__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact, int c_begin,
+                             int c_end, int T, SplitSmem<D> &sm, int *last_flag) {
   const int G = a.group;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
-
-  // per head: global max / sum and the per-split rescale factors
-  for (int h = w; h < G; h += kWaves) {
-    const float *ml = a.part_ml + (head0 + h) * a.nsplit * 2;
-    float mx = kNegInf;
-    for (int s = lane; s < nact; s += 64) mx = fmaxf(mx, load_agent(ml + 2 * s));
-    const float M = wave_max(mx);
-    float lsum = 0.f;
-    for (int s = lane; s < nact; s += 64) {
-      const float ms = load_agent(ml + 2 * s);
-      const float f = ms == kNegInf ? 0.f : fast_exp2(ms - M);
-      sm.f[h][s] = f;
-      lsum += f * load_agent(ml + 2 * s + 1);
-    }
-    const float L = wave_sum(lsum);
-    if (lane == 0) {
-      sm.M[h] = M;
-      sm.L[h] = L;
-    }
-  }
-  __syncthreads();
-
-  for (int item = threadIdx.x; item < G * D; item += kThreads) {
-    const int h = item / D, c = item % D;
-    const float *po = a.part_o + (head0 + h) * a.nsplit * D + c;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nact; ++s) acc += load_agent(po + (int64_t)s * D) * sm.f[h][s];
-    const float L = sm.L[h];
-    a.out[(head0 + h) * D + c] = L > 0.f ? acc / L : 0.f;
-  }
-  if (a.lse != nullptr && threadIdx.x < G) {
-    const float L = sm.L[threadIdx.x];
-    a.lse[head0 + threadIdx.x] = L > 0.f ? (sm.M[threadIdx.x] + __log2f(L)) * kLn2 : kNegInf;
-  }
-
-  if (a.sel_log != nullptr) {
-    const int64_t r0 = ((int64_t)b * a.num_kv_heads + g) * a.k;
-    for (int r = threadIdx.x; r < a.k; r += kThreads) a.sel_log[r0 + r] = a.sel[r0 + r];
-  }
-  if (a.stats == nullptr) return;
-
-  // block score: sum over the group's heads of the softmax mass of the block
-  const int N = (T + kBlockTokens - 1) / kBlockTokens;
-  const int nchunks = (T + kChunkTokens - 1) / kChunkTokens;
-  const int64_t stride = (int64_t)kChunksPerBlock * a.max_blocks * 2;
-  for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
-    float score = 0.f;
-    if (n < N) {
-      for (int h = 0; h < G; ++h) {
-        const float L = sm.L[h];
-        if (!(L > 0.f)) continue;
-        const float *st = a.stats + (head0 + h) * stride;
-        float mass = 0.f;
-        for (int c = n * kChunksPerBlock; c < (n + 1) * kChunksPerBlock && c < nchunks; ++c)
-          mass += load_agent(st + 2 * c + 1) * fast_exp2(load_agent(st + 2 * c) - sm.M[h]);
-        score += mass / L;
-      }
-      sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
-    }
-    if (a.score_out != nullptr)
-      a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = score;
-  }
-  if (a.idx_out != nullptr) {
-    __syncthreads();
-    select_topk(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
-  }
-}
-
-// Writes the workgroup partial from the four wavefront states in LDS, then
-// counts the workgroup's arrival; the last of the nact workgroups of (b, g)
-// runs the epilogue.  Returns true in that workgroup.
-template <int D>
-__device__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact,
-                             const float (*sm_m)[kMaxGroup], const float (*sm_l)[kMaxGroup],
-                             const float (*sm_o)[kMaxGroup][D], int *last_flag) {
-  for (int item = threadIdx.x; item < a.group * D; item += kThreads) {
-    const int h = item / D, c = item % D;
+  const __amdgpu_buffer_rsrc_t po = buffer(a.part_o + head0 * a.nsplit * D,
+                                           (uint32_t)(G * a.nsplit * D * 4));
+  for (int item = threadIdx.x; item < G * (D / 4); item += kThreads) {
+    const int h = item / (D / 4), c = 4 * (item % (D / 4));
     float m = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm_m[w][h]);
-    float o = 0.f, l = 0.f;
+    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm.m[w][h]);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = sm_m[w][h] == kNegInf ? 0.f : fast_exp2(sm_m[w][h] - m);
-      o += f * sm_o[w][h][c];
-      l += f * sm_l[w][h];
+      const float f = rescale(sm.m[w][h], m);
+      o += f * *reinterpret_cast<const f32x4 *>(&sm.o[w][h][c]);
+      l += f * sm.l[w][h];
     }
-    const int64_t row = ((int64_t)b * a.num_q_heads + g * a.group + h) * a.nsplit + s;
-    store_agent(a.part_o + row * D + c, o);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), po,
+                                           (uint32_t)(((h * a.nsplit + s) * D + c) * 4), 0,
+                                           kCoherent);
     if (c == 0) {
+      const int64_t row = (head0 + h) * a.nsplit + s;
       store_agent(a.part_ml + row * 2 + 0, m);
       store_agent(a.part_ml + row * 2 + 1, l);
     }
   }
-  // every store of this workgroup (partial and chunk statistics) completes
-  // before the arrival is counted; the last arrival then reads everyone's.
+  if (a.stats != nullptr) {
+    const int nb0 = c_begin / kChunksPerBlock;
+    const int nblk = (c_end - c_begin + kChunksPerBlock - 1) / kChunksPerBlock;
+    const int N = (T + kBlockTokens - 1) / kBlockTokens;
+    for (int item = threadIdx.x; item < G * nblk; item += kThreads) {
+      const int h = item / nblk, nl = item % nblk;
+      float m = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm.m[w][h]);
+      const float v = m == kNegInf ? 0.f : sm.bp[nl][h] * rescale(sm.bm[nl][h], m);
+      if (nb0 + nl < N) store_agent(a.stats + (head0 + h) * a.max_blocks + nb0 + nl, v);
+    }
+  }
+  // every store of this workgroup completes before the arrival is counted;
+  // the last arrival then reads everyone's.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -342,6 +336,128 @@ __device__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact,
   const bool last = *last_flag != 0;
   __syncthreads();  // the epilogue reuses the LDS of the split pass
   return last;
+}
+
+// Merges the nact split partials of (b, g) into out / lse; in full mode with
+// block masses also the block scores and the top-k.  Runs in the last
+// workgroup of (b, g) to finish its split pass.
+template <int D>
+__device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
+  const int G = a.group;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
+
+  // per head: global max / sum and the per-split rescale factors
+  for (int h = w; h < G; h += kWaves) {
+    const float *ml = a.part_ml + (head0 + h) * a.nsplit * 2;
+    float ms[kMaxSplits / 64], ls[kMaxSplits / 64];
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kMaxSplits / 64; ++j) {
+      const int s = lane + 64 * j;
+      ms[j] = s < nact ? load_agent(ml + 2 * s) : kNegInf;
+      ls[j] = s < nact ? load_agent(ml + 2 * s + 1) : 0.f;
+      mx = fmaxf(mx, ms[j]);
+    }
+    const float M = wave_max(mx);
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxSplits / 64; ++j) {
+      const int s = lane + 64 * j;
+      const float f = rescale(ms[j], M);
+      if (s < nact) sm.f[h][s] = f;
+      lsum += f * ls[j];
+    }
+    const float L = wave_sum(lsum);
+    if (lane == 0) {
+      sm.M[h] = M;
+      sm.L[h] = L;
+    }
+  }
+  __syncthreads();
+
+  // out: thread -> (head, 4 columns, stripe of splits); stripes summed in LDS
+  const int items = G * (D / 4);
+  const int stripes = items >= kThreads ? 1 : kThreads / items;
+  const __amdgpu_buffer_rsrc_t po = buffer(a.part_o + head0 * a.nsplit * D,
+                                           (uint32_t)(G * a.nsplit * D * 4));
+  for (int base = 0; base < items; base += kThreads) {
+    const int item = base + threadIdx.x % (items >= kThreads ? kThreads : items);
+    const int stripe = items >= kThreads ? 0 : threadIdx.x / items;
+    const int h = item / (D / 4), c = 4 * (item % (D / 4));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (item < items && stripe < stripes) {
+#pragma unroll 16
+      for (int s = stripe; s < nact; s += stripes)
+        acc += sm.f[h][s] * __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           po, (uint32_t)(((h * a.nsplit + s) * D + c) * 4), 0,
+                                           kCoherent));
+    }
+    if (stripes > 1) {
+      sm.red[threadIdx.x] = acc;
+      __syncthreads();
+      if (threadIdx.x < items) {
+        for (int st = 1; st < stripes; ++st) acc += sm.red[st * items + threadIdx.x];
+      }
+    }
+    if (threadIdx.x < (items >= kThreads ? kThreads : items) && item < items) {
+      const float L = sm.L[h];
+      const f32x4 o = L > 0.f ? acc * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4 *>(a.out + (head0 + h) * D + c) = o;
+    }
+  }
+  if (a.lse != nullptr && threadIdx.x < G) {
+    const float L = sm.L[threadIdx.x];
+    a.lse[head0 + threadIdx.x] = L > 0.f ? (sm.M[threadIdx.x] + __log2f(L)) * kLn2 : kNegInf;
+  }
+
+  if (a.sel_log != nullptr) {
+    const int64_t r0 = ((int64_t)b * a.num_kv_heads + g) * a.k;
+    for (int r = threadIdx.x; r < a.k; r += kThreads) a.sel_log[r0 + r] = a.sel[r0 + r];
+  }
+  if (a.stats == nullptr) return;
+
+  // block score: sum over the group's heads of the softmax mass of the block
+  // (mass stored relative to its split's max; f brings it to the head's max)
+  const int N = (T + kBlockTokens - 1) / kBlockTokens;
+  const int blocks_per_split = a.chunks_per_wg / kChunksPerBlock;
+  for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
+    float score = 0.f;
+    if (n < N) {
+      const int s = n / blocks_per_split;
+      for (int h = 0; h < G; ++h) {
+        const float L = sm.L[h];
+        if (L > 0.f) score += load_agent(a.stats + (head0 + h) * a.max_blocks + n) * sm.f[h][s] / L;
+      }
+      sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
+    }
+    if (a.score_out != nullptr)
+      a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = score;
+  }
+  if (a.idx_out != nullptr) {
+    __syncthreads();
+    select_topk(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
+  }
+}
+
+// Common prologue: range of the workgroup, early exits.  Returns false if the
+// workgroup has nothing to do.
+struct Range {
+  int T, C, c_begin, c_end, nact;
+};
+__device__ __forceinline__ bool wg_range(const AttnArgs &a, int s, int g, int b, int D, Range &r) {
+  r.T = clamp_ctx(scalar_load(a.ctx, b), a.max_blocks);
+  r.C = chunk_positions(r.T, a.sel, a.k);
+  if (r.C == 0) {
+    if (s == 0) write_empty(a, b, g, D);
+    return false;
+  }
+  r.c_begin = s * a.chunks_per_wg;
+  if (r.c_begin >= r.C) return false;
+  r.c_end = min(r.C, r.c_begin + a.chunks_per_wg);
+  r.nact = (r.C + a.chunks_per_wg - 1) / a.chunks_per_wg;
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -365,34 +481,27 @@ struct BfTile {
 };
 
 template <int D>
-union BfSmem {
-  struct {
-    float m[kWaves][kMaxGroup];
-    float l[kWaves][kMaxGroup];
-    float o[kWaves][kMaxGroup][D];
-  } main;
-  EpiSmem epi;
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_split_bf16(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_split_bf16(
+    AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int T = clamp_ctx(a.ctx[b], a.max_blocks);
-  const int C = chunk_positions(T, a.sel, a.k);
-  __shared__ BfSmem<D> sm;
+  __shared__ KernelSmem<D> sm;
   __shared__ int last_flag;
-  if (C == 0) {
-    if (s == 0) write_empty(a, b, g, D);
-    return;
-  }
-  const int c_begin = s * a.chunks_per_wg;
-  if (c_begin >= C) return;
-  const int c_end = min(C, c_begin + a.chunks_per_wg);
-  const int nact = (C + a.chunks_per_wg - 1) / a.chunks_per_wg;
+  Range r;
+  if (!wg_range(a, s, g, b, D, r)) return;
+  const int T = r.T, c_begin = r.c_begin, c_end = r.c_end;
+  const bool blocked = a.sel == nullptr;
+  const bool want_mass = a.stats != nullptr;
 
   const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int quad = lane >> 4, m16 = lane & 15;
   const int G = a.group;
+
+  if (want_mass)
+    for (int i = threadIdx.x; i < kMaxWgBlocks * kMaxGroup; i += kThreads) {
+      sm.split.bm[i / kMaxGroup][i % kMaxGroup] = kNegInf;
+      sm.split.bp[i / kMaxGroup][i % kMaxGroup] = 0.f;
+    }
+  __syncthreads();
 
   bf16x8 qop[D / 32];
   {
@@ -406,7 +515,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f, bmass = 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -417,25 +526,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // per-lane byte offsets inside a chunk's K rows / V columns (chunk-invariant)
   const uint32_t k_lane = (uint32_t)(((8 * (m16 >> 2) + (m16 & 3)) * D + 8 * quad) * 2);
   const uint32_t v_lane = (uint32_t)((m16 * kBlockTokens + 8 * quad) * 2);
-  float *stats_row = a.stats ? a.stats + ((int64_t)b * a.num_q_heads + g * G + m16) *
-                                             (int64_t)(kChunksPerBlock * a.max_blocks) * 2
-                             : nullptr;
 
   // Issues the 16-byte loads of chunk `pos` into t through buffer resources
   // spanning just that chunk; returns its valid token count.  A position past
   // the range or without a readable page gets an empty resource: the loads
   // return zeros without touching memory, so every path issues the same loads
   // and the register tiles never need copying.
-  auto issue = [&](BfTile<D> &t, int pos) -> int {
+  auto issue = [&](BfTile<D> &t, int pos, bool live) -> int {
     int page = 0, sub = 0, valid = 0;
-    bool ok = false;
-    if (pos < c_end) {
-      ok = resolve_chunk(a, b, g, T, pos, page, sub, valid);
-      if (!ok && stats_row != nullptr && quad == 0 && m16 < G) {  // unreadable page: no mass
-        store_agent(stats_row + 2 * pos + 0, kNegInf);
-        store_agent(stats_row + 2 * pos + 1, 0.f);
-      }
-    }
+    const bool ok = live && pos < c_end && resolve_chunk(a, b, g, T, pos, page, sub, valid);
     if (!ok) {
       page = 0;
       sub = 0;
@@ -444,11 +543,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t tile = (int64_t)page * Hkv + g;
     const char *kb = kpool + (tile * kBlockTokens + sub * kChunkTokens) * D * 2;
     const char *vb = vpool + (tile * D * kBlockTokens + sub * kChunkTokens) * 2;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(kb), (short)0, ok ? kChunkTokens * D * 2 : 0, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(vb), (short)0, ok ? (D - 1) * kBlockTokens * 2 + kChunkTokens * 2 : 0,
-        kBufferFlags);
+    const __amdgpu_buffer_rsrc_t krs = buffer(kb, ok ? kChunkTokens * D * 2 : 0);
+    const __amdgpu_buffer_rsrc_t vrs =
+        buffer(vb, ok ? (D - 1) * kBlockTokens * 2 + kChunkTokens * 2 : 0);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -460,7 +557,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     return valid;
   };
 
-  auto consume = [&](const BfTile<D> &t, int pos, int valid) {
+  auto consume = [&](const BfTile<D> &t, int valid) {
     f32x4 sacc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -496,11 +593,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
+    bmass = bmass * alpha + ps;
     m_run = m_new;
-    if (stats_row != nullptr && quad == 0 && m16 < G) {
-      store_agent(stats_row + 2 * pos + 0, m_new);
-      store_agent(stats_row + 2 * pos + 1, ps);
-    }
     float al[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * quad + r);
@@ -522,32 +616,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
+  // block-mass bookkeeping of the i-th chunk (full mode with scores): the
+  // mass restarts with each block and is recorded after every chunk.
+  auto step = [&](const BfTile<D> &t, int i, int valid) {
+    if (want_mass && i % kChunksPerBlock == 0) bmass = 0.f;
+    if (valid > 0) consume(t, valid);
+    if (want_mass && quad == 0 && m16 < G) {
+      const int nl = w + kWaves * (i / kChunksPerBlock);
+      sm.split.bm[nl][m16] = m_run;
+      sm.split.bp[nl][m16] = bmass;
+    }
+  };
+
   // Two register tiles: the next chunk's loads are in flight while the
   // current one is consumed.
   BfTile<D> ta, tb;
-  int pos = c_begin + w;
-  int va = issue(ta, pos);
-  while (pos < c_end) {
-    const int vb = issue(tb, pos + kWaves);
-    if (va > 0) consume(ta, pos, va);
-    pos += kWaves;
-    if (pos >= c_end) break;
-    va = issue(ta, pos + kWaves);
-    if (vb > 0) consume(tb, pos, vb);
-    pos += kWaves;
+  int i = 0;
+  bool live = chunk_live(blocked, c_begin, c_end, w, 0);
+  int va = issue(ta, chunk_of(blocked, c_begin, w, 0), live);
+  while (live) {
+    const bool live_b = chunk_live(blocked, c_begin, c_end, w, i + 1);
+    const int vb = issue(tb, chunk_of(blocked, c_begin, w, i + 1), live_b);
+    step(ta, i, va);
+    ++i;
+    if (!live_b) break;
+    const bool live_a = chunk_live(blocked, c_begin, c_end, w, i + 1);
+    va = issue(ta, chunk_of(blocked, c_begin, w, i + 1), live_a);
+    step(tb, i, vb);
+    ++i;
+    live = live_a;
   }
 
   if (quad == 0) {
-    sm.main.m[w][m16] = m_run;
-    sm.main.l[w][m16] = l_run;
+    sm.split.m[w][m16] = m_run;
+    sm.split.l[w][m16] = l_run;
   }
 #pragma unroll
   for (int n = 0; n < D / 16; ++n)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.main.o[w][4 * quad + r][16 * n + m16] = acc[n][r];
+    for (int r = 0; r < 4; ++r) sm.split.o[w][4 * quad + r][16 * n + m16] = acc[n][r];
   __syncthreads();
-  if (!finish_split<D>(a, b, g, s, nact, sm.main.m, sm.main.l, sm.main.o, &last_flag)) return;
-  epilogue<D>(a, b, g, T, nact, sm.epi);
+  if (!finish_split<D>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
+  epilogue<D>(a, b, g, T, r.nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -556,36 +666,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // group; p.V runs with lane i owning columns i and i+64.
 // ---------------------------------------------------------------------------
 template <int D>
-union F32Smem {
-  struct {
-    float q[kMaxGroup][D];
-    float m[kWaves][kMaxGroup];
-    float l[kWaves][kMaxGroup];
-    float o[kWaves][kMaxGroup][D];
-  } main;
-  EpiSmem epi;
-};
-
-template <int D>
 __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int T = clamp_ctx(a.ctx[b], a.max_blocks);
-  const int C = chunk_positions(T, a.sel, a.k);
-  __shared__ F32Smem<D> sm;
+  __shared__ KernelSmem<D> sm;
+  __shared__ float q_s[kMaxGroup][D];
   __shared__ int last_flag;
-  if (C == 0) {
-    if (s == 0) write_empty(a, b, g, D);
-    return;
-  }
-  const int c_begin = s * a.chunks_per_wg;
-  if (c_begin >= C) return;
-  const int c_end = min(C, c_begin + a.chunks_per_wg);
-  const int nact = (C + a.chunks_per_wg - 1) / a.chunks_per_wg;
+  Range r;
+  if (!wg_range(a, s, g, b, D, r)) return;
+  const int T = r.T, c_begin = r.c_begin, c_end = r.c_end;
+  const bool blocked = a.sel == nullptr;
+  const bool want_mass = a.stats != nullptr;
 
   constexpr int CPL = D / 64;  // output columns per lane
   const int G = a.group;
   const float *qg = static_cast<const float *>(a.q) + ((int64_t)b * a.num_q_heads + g * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) sm.main.q[i / D][i % D] = qg[i];
+  for (int i = threadIdx.x; i < G * D; i += kThreads) q_s[i / D][i % D] = qg[i];
+  if (want_mass)
+    for (int i = threadIdx.x; i < kMaxWgBlocks * kMaxGroup; i += kThreads) {
+      sm.split.bm[i / kMaxGroup][i % kMaxGroup] = kNegInf;
+      sm.split.bp[i / kMaxGroup][i % kMaxGroup] = 0.f;
+    }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
@@ -594,101 +694,103 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   const float *vpool = static_cast<const float *>(a.v_pool);
   const int Hkv = a.num_kv_heads;
 
-  float m_run[kMaxGroup], l_run[kMaxGroup], acc[kMaxGroup][CPL];
+  float m_run[kMaxGroup], l_run[kMaxGroup], bmass[kMaxGroup], acc[kMaxGroup][CPL];
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     m_run[h] = kNegInf;
     l_run[h] = 0.f;
+    bmass[h] = 0.f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) acc[h][j] = 0.f;
   }
 
-  for (int pos = c_begin + w; pos < c_end; pos += kWaves) {
+  for (int i = 0; chunk_live(blocked, c_begin, c_end, w, i); ++i) {
+    const int pos = chunk_of(blocked, c_begin, w, i);
+    if (want_mass && i % kChunksPerBlock == 0)
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) bmass[h] = 0.f;
     int page, sub, valid;
-    if (!resolve_chunk(a, b, g, T, pos, page, sub, valid)) {
-      if (a.stats != nullptr && lane < G) {  // unreadable page: no mass
-        float *st = a.stats + ((int64_t)b * a.num_q_heads + g * G + lane) *
-                                  (int64_t)(kChunksPerBlock * a.max_blocks) * 2;
-        store_agent(st + 2 * pos + 0, kNegInf);
-        store_agent(st + 2 * pos + 1, 0.f);
+    if (pos < c_end && resolve_chunk(a, b, g, T, pos, page, sub, valid)) {
+      const int64_t tile = (int64_t)page * Hkv + g;
+      const float *krow =
+          kpool + (tile * kBlockTokens + sub * kChunkTokens + t) * D + half * (D / 2);
+      float sc[kMaxGroup];
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) sc[h] = 0.f;
+      if (t < valid) {
+        for (int c = 0; c < D / 2; c += 4) {
+          const float4 kv = *reinterpret_cast<const float4 *>(krow + c);
+#pragma unroll
+          for (int h = 0; h < kMaxGroup; ++h) {
+            if (h < G) {
+              const float *qh = &q_s[h][half * (D / 2) + c];
+              sc[h] += qh[0] * kv.x + qh[1] * kv.y + qh[2] * kv.z + qh[3] * kv.w;
+            }
+          }
+        }
       }
-      continue;
-    }
-    const int64_t tile = (int64_t)page * Hkv + g;
-    const float *krow = kpool + (tile * kBlockTokens + sub * kChunkTokens + t) * D + half * (D / 2);
-    float sc[kMaxGroup];
+      float p[kMaxGroup], alpha[kMaxGroup];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) sc[h] = 0.f;
-    if (t < valid) {
-      for (int c = 0; c < D / 2; c += 4) {
-        const float4 kv = *reinterpret_cast<const float4 *>(krow + c);
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h >= G) continue;
+        const float tot = sc[h] + __shfl_xor(sc[h], 32);
+        const float x = t < valid ? tot * a.scale_log2 : kNegInf;
+        float mx = x;
 #pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-          if (h < G) {
-            const float *qh = &sm.main.q[h][half * (D / 2) + c];
-            sc[h] += qh[0] * kv.x + qh[1] * kv.y + qh[2] * kv.z + qh[3] * kv.w;
+        for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        const float m_new = fmaxf(m_run[h], mx);
+        alpha[h] = fast_exp2(m_run[h] - m_new);
+        p[h] = fast_exp2(x - m_new);
+        float ps = p[h];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) ps += __shfl_xor(ps, o);
+        l_run[h] = l_run[h] * alpha[h] + ps;
+        bmass[h] = bmass[h] * alpha[h] + ps;
+        m_run[h] = m_new;
+      }
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const float *vrow = vpool + (tile * D + lane + 64 * j) * kBlockTokens + sub * kChunkTokens;
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h)
+          if (h < G) acc[h][j] *= alpha[h];
+        for (int tt = 0; tt < kChunkTokens; tt += 4) {
+          const float4 v4 = *reinterpret_cast<const float4 *>(vrow + tt);
+          const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float vv = tt + e < valid ? ve[e] : 0.f;
+#pragma unroll
+            for (int h = 0; h < kMaxGroup; ++h)
+              if (h < G) acc[h][j] += __shfl(p[h], tt + e) * vv;
           }
         }
       }
     }
-    float p[kMaxGroup], alpha[kMaxGroup];
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h >= G) continue;
-      const float tot = sc[h] + __shfl_xor(sc[h], 32);
-      const float x = t < valid ? tot * a.scale_log2 : kNegInf;
-      float mx = x;
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const float m_new = fmaxf(m_run[h], mx);
-      alpha[h] = fast_exp2(m_run[h] - m_new);
-      p[h] = fast_exp2(x - m_new);
-      float ps = p[h];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) ps += __shfl_xor(ps, o);
-      l_run[h] = l_run[h] * alpha[h] + ps;
-      m_run[h] = m_new;
-      if (a.stats != nullptr && lane == 0) {
-        float *st = a.stats + ((int64_t)b * a.num_q_heads + g * G + h) *
-                                  (int64_t)(kChunksPerBlock * a.max_blocks) * 2;
-        store_agent(st + 2 * pos + 0, m_new);
-        store_agent(st + 2 * pos + 1, ps);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const float *vrow = vpool + (tile * D + lane + 64 * j) * kBlockTokens + sub * kChunkTokens;
+    if (want_mass && lane == 0) {
+      const int nl = w + kWaves * (i / kChunksPerBlock);
 #pragma unroll
       for (int h = 0; h < kMaxGroup; ++h)
-        if (h < G) acc[h][j] *= alpha[h];
-      for (int tt = 0; tt < kChunkTokens; tt += 4) {
-        const float4 v4 = *reinterpret_cast<const float4 *>(vrow + tt);
-        const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float vv = tt + e < valid ? ve[e] : 0.f;
-#pragma unroll
-          for (int h = 0; h < kMaxGroup; ++h)
-            if (h < G) acc[h][j] += __shfl(p[h], tt + e) * vv;
+        if (h < G) {
+          sm.split.bm[nl][h] = m_run[h];
+          sm.split.bp[nl][h] = bmass[h];
         }
-      }
     }
   }
 
-  __syncthreads();  // q no longer read; the merge arrays follow it in LDS
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h >= G) continue;
     if (lane == 0) {
-      sm.main.m[w][h] = m_run[h];
-      sm.main.l[w][h] = l_run[h];
+      sm.split.m[w][h] = m_run[h];
+      sm.split.l[w][h] = l_run[h];
     }
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) sm.main.o[w][h][lane + 64 * j] = acc[h][j];
+    for (int j = 0; j < CPL; ++j) sm.split.o[w][h][lane + 64 * j] = acc[h][j];
   }
   __syncthreads();
-  if (!finish_split<D>(a, b, g, s, nact, sm.main.m, sm.main.l, sm.main.o, &last_flag)) return;
-  epilogue<D>(a, b, g, T, nact, sm.epi);
+  if (!finish_split<D>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
+  epilogue<D>(a, b, g, T, r.nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
