@@ -2,9 +2,12 @@
 
 A step is one hybrid decode step of every layer of the workload (reset layers:
 full attention + block scores + top-k; reuse layers: attention over the
-carried blocks) for the whole batch, inputs resident in HBM.  Also timed: the
-plain full-attention step (every layer full attention, no scores) and the
-all-reset step (every layer full attention + scores + top-k).
+carried blocks) for the whole batch, inputs resident in HBM, launched in layer
+order on one stream.  `value` times the step replayed as one HIP graph (the
+form a decode loop with static shapes runs); the eager step rate is reported
+beside it.  Also timed: the plain full-attention step (every layer full
+attention, no scores) and the all-reset step (every layer full attention +
+scores + top-k).
 
 Prints one JSON line.  `value` is hybrid decode steps/s.  `roofline` covers
 the dominant kernel (full split attention of the reset layers): algorithmic
@@ -82,6 +85,30 @@ def timed(fn, steps, warmup, torch, timers, hylra):
     return ms, kern
 
 
+def graph_timed(fn, steps, warmup, torch):
+    """Capture one call of fn (all its launches) in a HIP graph and time
+    `steps` replays.  Returns (ms per step, graph)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps, graph
+
+
 def cpu_baseline(wl, layers, src, k, budget_s):
     """Oracle timed on the host over a prefix of the step's layers; the step
     time is extrapolated from the mean reset-layer and reuse-layer times."""
@@ -145,21 +172,25 @@ def main():
 
     hybrid = hylra.PolicyPlan(layers, src, k)
     ALL = (hylra.KERNEL_FULL_ATTN, hylra.KERNEL_SPARSE_ATTN)
-    ms_h, kern = timed(hybrid.run, args.steps, args.warmup, torch, ALL, hylra)
-    result_extra = {}
+    # eager steps with per-kernel HIP events (per-layer latency, roofline)
+    ms_eager, kern = timed(hybrid.run, args.steps, args.warmup, torch, ALL, hylra)
+    # the step as one HIP graph (how a decode loop replays a static step): value
+    ms_h, _ = graph_timed(hybrid.run, args.steps, args.warmup, torch)
+    result_extra = {"eager_steps_per_s": 1000.0 / ms_eager, "eager_ms_per_step": ms_eager}
     if not args.skip_baselines:
         full = hylra.FullPlan(layers)
-        ms_f, kern_f = timed(full.run, args.steps, args.warmup, torch,
-                             (hylra.KERNEL_FULL_ATTN,), hylra)
+        _, kern_f = timed(full.run, args.steps, args.warmup, torch,
+                          (hylra.KERNEL_FULL_ATTN,), hylra)
+        ms_f, _ = graph_timed(full.run, args.steps, args.warmup, torch)
         allreset = hylra.PolicyPlan(layers, list(range(L)), k)
-        ms_a, _ = timed(allreset.run, args.steps, args.warmup, torch, (), hylra)
-        result_extra = {
+        ms_a, _ = graph_timed(allreset.run, args.steps, args.warmup, torch)
+        result_extra.update({
             "full_steps_per_s": 1000.0 / ms_f,
             "full_ms_per_step": ms_f,
             "all_reset_steps_per_s": 1000.0 / ms_a,
             "hybrid_over_full": ms_f / ms_h,
             "full_attn_no_scores_us": kern_f[hylra.KERNEL_FULL_ATTN][0] * 1e3,
-        }
+        })
 
     B, Hkv, T, d = wl.batch, wl.num_kv_heads, wl.ctx, wl.head_dim
     elt = 4 if wl.dtype == "f32" else 2

@@ -300,3 +300,43 @@ def test_run_policy_llama3_8b_32k_sampled(H):
     assert torch.equal(idx2, idx_log)
     for a, b in zip(outs, outs2):
         assert torch.equal(a, b)
+
+
+def test_run_policy_graph_replays_match_eager(H):
+    """The whole step captured in a HIP graph: every replay, with eager work
+    and synchronisations in between, is bit-identical to the eager step."""
+    say("run_policy graph replay")
+    ctx = (5000, 1200)
+    layers = [gpu_layer("bf16", ctx, 32, 8, 128, seed=300 + 16 * l, hot=[[3, 9], [1]])
+              for l in range(6)]
+    src = [0, 0, 0, 3, 3, 5]
+    k = 8
+    eager = H.PolicyPlan(layers, src, k, idx_log=torch.full((6, 2, 8, k), -2, dtype=torch.int32,
+                                                            device="cuda"))
+    ref_out, ref_lse = eager.run()
+    ref_out = [o.clone() for o in ref_out]
+    ref_lse = [l.clone() for l in ref_lse]
+    ref_idx = eager.idx_log.clone()
+    plan = H.PolicyPlan(layers, src, k, idx_log=torch.full((6, 2, 8, k), -2, dtype=torch.int32,
+                                                           device="cuda"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.run()
+    for rep in range(4):
+        for o in plan.out:
+            o.fill_(float("nan"))
+        plan.idx_log.fill_(-3)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(plan.out, ref_out):
+            assert torch.equal(a, b), "replay %d out" % rep
+        for a, b in zip(plan.lse, ref_lse):
+            assert torch.equal(a, b), "replay %d lse" % rep
+        assert torch.equal(plan.idx_log, ref_idx), "replay %d idx" % rep
+        eager.run()  # eager work between replays
+        torch.cuda.synchronize()
