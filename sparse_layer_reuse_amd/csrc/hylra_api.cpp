@@ -200,20 +200,19 @@ hylra_status run_sparse(const hylra_shape *s, const void *q, const hylra_kv *kv,
 
 namespace hylra {
 
-// Split plans: about 512 workgroups per launch (two resident per compute
-// unit on a 256-CU part), each wavefront taking an equal share of chunks, and
-// at most kMaxSplits workgroups per (sequence, KV head) for the epilogue.
-constexpr long kTargetWorkgroups = 512;
+// Split plans: about 256 workgroups per launch (one 8-wavefront workgroup
+// resident per compute unit on a 256-CU part).  Full mode: a multiple of
+// 4 * 8 chunks per workgroup, so every wavefront takes whole 128-token blocks;
+// sparse mode: a multiple of 8 chunks.  At most kMaxSplits workgroups per
+// (sequence, KV head) and kMaxWgChunks chunks per workgroup.
+constexpr long kTargetWorkgroups = 256;
 
-static SplitPlan make_plan(long chunks_per_seq, long rows) {
+static SplitPlan make_plan(long chunks_per_seq, long rows, long unit) {
   long cpw = (rows * chunks_per_seq + kTargetWorkgroups - 1) / kTargetWorkgroups;
   const long min_cpw = (chunks_per_seq + kMaxSplits - 1) / kMaxSplits;
   if (cpw < min_cpw) cpw = min_cpw;
-  cpw = (cpw + 3) / 4 * 4;
-  if (cpw < 4) cpw = 4;
-  // longer ranges would outgrow the per-workgroup block statistics in LDS;
-  // min_cpw <= 128 always (at most 4 * kMaxBlocks chunks over kMaxSplits)
-  if (cpw > kMaxWgChunks) cpw = kMaxWgChunks;
+  cpw = (cpw + unit - 1) / unit * unit;
+  if (cpw > kMaxWgChunks) cpw = kMaxWgChunks;  // min_cpw <= 128 always
   SplitPlan p;
   p.chunks_per_wg = (int)cpw;
   p.nsplit = (int)((chunks_per_seq + cpw - 1) / cpw);
@@ -221,12 +220,14 @@ static SplitPlan make_plan(long chunks_per_seq, long rows) {
 }
 
 SplitPlan plan_full(int batch, int num_kv_heads, int max_blocks) {
-  return make_plan((long)kChunksPerBlock * max_blocks, (long)batch * num_kv_heads);
+  return make_plan((long)kChunksPerBlock * max_blocks, (long)batch * num_kv_heads,
+                   (long)kChunksPerBlock * kWavesPerGroup);
 }
 
 SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k) {
   const long keff = k < max_blocks ? k : max_blocks;
-  return make_plan((long)kChunksPerBlock * (keff > 0 ? keff : 1), (long)batch * num_kv_heads);
+  return make_plan((long)kChunksPerBlock * (keff > 0 ? keff : 1), (long)batch * num_kv_heads,
+                   (long)kWavesPerGroup);
 }
 
 }  // namespace hylra

@@ -14,8 +14,9 @@ constexpr int kMaxBlocks = 8192;   // blocks per sequence (1M tokens)
 constexpr int kMaxSplits = 256;    // workgroups per (sequence, KV head)
 constexpr int kCounterSlots = 65536;  // (sequence, KV head) arrival counters in a workspace
 constexpr int kMaxWgChunks = 256;     // chunk positions per workgroup (64 blocks)
+constexpr int kWavesPerGroup = 8;     // wavefronts per workgroup (one workgroup per CU)
 
-// Work split of one attention launch: each workgroup (4 wavefronts) takes
+// Work split of one attention launch: each workgroup (8 wavefronts) takes
 // `chunks_per_wg` consecutive 32-token chunk positions of one (sequence, KV
 // head); `nsplit` workgroups cover the longest sequence.
 struct SplitPlan {

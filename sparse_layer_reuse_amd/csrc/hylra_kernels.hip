@@ -37,8 +37,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = kWavesPerGroup;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxWgBlocks = kMaxWgChunks / kChunksPerBlock;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -126,33 +126,89 @@ __device__ __forceinline__ bool chunk_live(bool blocked, int c_begin, int c_end,
                  : c_begin + w + kWaves * i < c_end;
 }
 
+// Wavefront reductions on DPP lane permutes (quad perms, row mirrors, row
+// broadcasts of lanes 15 / 31): each step is a VALU op, far cheaper in
+// latency than a ds_bpermute shuffle.  The result is read from lane 63.
+constexpr int kDppQuad1032 = 0xb1, kDppQuad2301 = 0x4e, kDppRowHalfMirror = 0x141,
+              kDppRowMirror = 0x140, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143,
+              kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118;
+
+template <int ctrl, int row_mask = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, ctrl, row_mask, 0xf, false);
+}
+template <int ctrl, int row_mask = 0xf>
+__device__ __forceinline__ float dpp_f32(float old, float src) {
+  return __builtin_bit_cast(float, dpp_u32<ctrl, row_mask>(__builtin_bit_cast(uint32_t, old),
+                                                          __builtin_bit_cast(uint32_t, src)));
+}
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppQuad1032>(v, v));
+  v = fmaxf(v, dpp_f32<kDppQuad2301>(v, v));
+  v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v, v));
+  v = fmaxf(v, dpp_f32<kDppRowBcast15, 0xa>(v, v));
+  v = fmaxf(v, dpp_f32<kDppRowBcast31, 0xc>(v, v));
+  return lane63(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f32<kDppQuad1032>(0.f, v);
+  v += dpp_f32<kDppQuad2301>(0.f, v);
+  v += dpp_f32<kDppRowHalfMirror>(0.f, v);
+  v += dpp_f32<kDppRowMirror>(0.f, v);
+  v += dpp_f32<kDppRowBcast15, 0xa>(0.f, v);
+  v += dpp_f32<kDppRowBcast31, 0xc>(0.f, v);
+  return lane63(v);
 }
 
-// Exclusive prefix sum over the 256 threads' values.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *tmp) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  __syncthreads();
-  if (lane == 63) tmp[w] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int i = 0; i < w; ++i) base += tmp[i];
-  return base + inc - v;
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp_u32<kDppQuad1032>(0u, v);
+  v |= dpp_u32<kDppQuad2301>(0u, v);
+  v |= dpp_u32<kDppRowHalfMirror>(0u, v);
+  v |= dpp_u32<kDppRowMirror>(0u, v);
+  v |= dpp_u32<kDppRowBcast15, 0xa>(0u, v);
+  v |= dpp_u32<kDppRowBcast31, 0xc>(0u, v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// LDS of the split pass: the four wavefront states and the block masses.
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  v &= dpp_u32<kDppQuad1032>(~0u, v);
+  v &= dpp_u32<kDppQuad2301>(~0u, v);
+  v &= dpp_u32<kDppRowHalfMirror>(~0u, v);
+  v &= dpp_u32<kDppRowMirror>(~0u, v);
+  v &= dpp_u32<kDppRowBcast15, 0xa>(~0u, v);
+  v &= dpp_u32<kDppRowBcast31, 0xc>(~0u, v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum over the 64 lanes: DPP shifts within rows of 16, then
+// the row totals (lanes 15, 31, 47) are added as scalars.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = (uint32_t)v;
+  x += dpp_u32<kDppRowShr1>(0u, x) * ((lane & 15) >= 1);
+  x += dpp_u32<kDppRowShr2>(0u, x) * ((lane & 15) >= 2);
+  x += dpp_u32<kDppRowShr4>(0u, x) * ((lane & 15) >= 4);
+  x += dpp_u32<kDppRowShr8>(0u, x) * ((lane & 15) >= 8);
+  const int r0 = __builtin_amdgcn_readlane((int)x, 15);
+  const int r1 = __builtin_amdgcn_readlane((int)x, 31);
+  const int r2 = __builtin_amdgcn_readlane((int)x, 47);
+  const int row = lane >> 4;
+  const int base = row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2;
+  return (int)x + base;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// LDS of the split pass: the wavefront states and the block masses.
 template <int D>
 struct SplitSmem {
   float m[kWaves][kMaxGroup];
@@ -170,89 +226,98 @@ struct EpiSmem {
   f32x4 red[kThreads];
   uint32_t keys[kMaxBlocks];
   int hist[256];
-  int scan[kWaves];
-  int pick_digit;
-  int pick_remaining;
 };
+
+// Selects the k_eff = min(k, N) largest keys[0..N) (unsigned compare), equal
+// keys going to the lower index, and writes their indices in ascending order
+// to out[0..k_eff), -1 after.  Run by ONE wavefront (no workgroup barrier):
+// keys must already be in LDS and visible to it.  Radix select over 4 x 8
+// bits (digits shared by every key are skipped) with a histogram private to
+// the wavefront finds the k_eff-th largest key `thr`; keys above thr are
+// taken, keys equal to thr in index order until k_eff (compaction by rows of
+// 64 blocks with ballots).
+__device__ __forceinline__ void select_topk_wave(EpiSmem &sm, int N, int k, int32_t *out) {
+  const int lane = threadIdx.x & 63;
+  const int keff = k < N ? k : N;
+  if (keff == N) {  // every block is selected (also N == 0)
+    for (int r = lane; r < k; r += 64) out[r] = r < N ? r : -1;
+    return;
+  }
+  uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+  for (int n = lane; n < N; n += 64) {
+    kor |= sm.keys[n];
+    kand &= sm.keys[n];
+  }
+  kor = wave_or(kor);
+  kand = wave_and(kand);
+  const uint32_t common = ~(kor ^ kand);
+  int *hist = sm.hist;
+
+  uint32_t prefix = 0u, mask = 0u;
+  int remaining = keff;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t dmask = 255u << shift;
+    if ((common & dmask) == dmask) {  // every key has the same digit here
+      prefix |= kand & dmask;
+      mask |= dmask;
+      continue;
+    }
+    *reinterpret_cast<u32x4 *>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    for (int n = lane; n < N; n += 64) {
+      const uint32_t kv = sm.keys[n];
+      if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // lane l holds bins 255-4l .. 252-4l (descending); find the bin where the
+    // count of keys from the top reaches `remaining`
+    const u32x4 hv = *reinterpret_cast<const u32x4 *>(&hist[252 - 4 * lane]);
+    const int c[4] = {(int)hv[3], (int)hv[2], (int)hv[1], (int)hv[0]};
+    const int tot = c[0] + c[1] + c[2] + c[3];
+    int above = wave_inclusive_scan(tot) - tot;
+    int digit = -1, rem = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (above < remaining && remaining <= above + c[i]) {
+        digit = 255 - 4 * lane - i;
+        rem = remaining - above;
+      }
+      above += c[i];
+    }
+    const int leader = __builtin_ctzll(__ballot(digit >= 0));
+    prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, leader) << shift;
+    mask |= dmask;
+    remaining = __builtin_amdgcn_readlane(rem, leader);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // bins are reused by the next pass
+  }
+  const uint32_t thr = prefix;
+  const int need_eq = remaining;
+
+  int taken = 0, eq_before = 0;
+  for (int base = 0; base < N; base += 64) {
+    const int n = base + lane;
+    const uint32_t kv = n < N ? sm.keys[n] : 0u;
+    const bool is_gt = n < N && kv > thr;
+    const bool is_eq = n < N && kv == thr;
+    const uint64_t eqm = __ballot(is_eq);
+    const bool sel = is_gt || (is_eq && eq_before + lanes_below(eqm) < need_eq);
+    const uint64_t selm = __ballot(sel);
+    if (sel) out[taken + lanes_below(selm)] = n;
+    taken += __builtin_popcountll(selm);
+    eq_before += __builtin_popcountll(eqm);
+  }
+  for (int r = keff + lane; r < k; r += 64) out[r] = -1;
+}
 
 template <int D>
 union KernelSmem {
   SplitSmem<D> split;
   EpiSmem epi;
 };
-
-// Selects the k_eff = min(k, N) largest keys[0..N) (unsigned compare), equal
-// keys going to the lower index, and writes their indices in ascending order
-// to out[0..k_eff), -1 after.  keys must be in LDS and visible to all threads.
-// Radix select over 4 x 8 bits finds the k_eff-th largest key `thr`; keys
-// above thr are taken, keys equal to thr in index order until k_eff.
-__device__ void select_topk(EpiSmem &sm, int N, int k, int32_t *out) {
-  const int keff = k < N ? k : N;
-  if (keff == N) {  // every block is selected (also N == 0)
-    for (int r = threadIdx.x; r < k; r += kThreads) out[r] = r < N ? r : -1;
-    return;
-  }
-  uint32_t prefix = 0u, mask = 0u;
-  int remaining = keff;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    __syncthreads();
-    sm.hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int n = threadIdx.x; n < N; n += kThreads)
-      if ((sm.keys[n] & mask) == prefix) atomicAdd(&sm.hist[(sm.keys[n] >> shift) & 255u], 1);
-    __syncthreads();
-    const int rb = 255 - threadIdx.x;  // bins in descending order
-    const int cnt = sm.hist[rb];
-    const int above = block_exclusive_scan(cnt, sm.scan);  // keys in bins > rb
-    if (above < remaining && remaining <= above + cnt) {
-      sm.pick_digit = rb;
-      sm.pick_remaining = remaining - above;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sm.pick_digit << shift;
-    mask |= 255u << shift;
-    remaining = sm.pick_remaining;
-  }
-  const uint32_t thr = prefix;
-  const int need_eq = remaining;
-
-  // contiguous range per thread keeps index order for the scans
-  const int per = (N + kThreads - 1) / kThreads;
-  const int lo = threadIdx.x * per, hi = min(N, lo + per);
-  int eq_cnt = 0;
-  for (int n = lo; n < hi; ++n) eq_cnt += sm.keys[n] == thr;
-  const int eq_rank = block_exclusive_scan(eq_cnt, sm.scan);
-  int sel_cnt = 0;
-  {
-    int r = eq_rank;
-    for (int n = lo; n < hi; ++n) {
-      const uint32_t kv = sm.keys[n];
-      if (kv > thr) {
-        ++sel_cnt;
-      } else if (kv == thr) {
-        if (r < need_eq) ++sel_cnt;
-        ++r;
-      }
-    }
-  }
-  int pos = block_exclusive_scan(sel_cnt, sm.scan);
-  {
-    int r = eq_rank;
-    for (int n = lo; n < hi; ++n) {
-      const uint32_t kv = sm.keys[n];
-      bool take = false;
-      if (kv > thr) {
-        take = true;
-      } else if (kv == thr) {
-        take = r < need_eq;
-        ++r;
-      }
-      if (take) out[pos++] = n;
-    }
-  }
-  for (int r = keff + threadIdx.x; r < k; r += kThreads) out[r] = -1;
-}
 
 // Outputs of a (b, g) with no chunk to attend (empty context).
 __device__ void write_empty(const AttnArgs &a, int b, int g, int D) {
@@ -341,11 +406,44 @@ __device__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact, i
 // Merges the nact split partials of (b, g) into out / lse; in full mode with
 // block masses also the block scores and the top-k.  Runs in the last
 // workgroup of (b, g) to finish its split pass.
+//
+// out: thread -> (head h, 4 columns c) item and a stripe of the splits.  The
+// first batch of partial outputs and the first block masses are loaded before
+// the (max, sum) pass, so the loads travel together.
 template <int D>
 __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
+  constexpr int kBatch = 8;
   const int G = a.group;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
+  const int items = G * (D / 4);  // <= kThreads
+  const int stripes = kThreads / items;
+  const int item = threadIdx.x % items, stripe = threadIdx.x / items;
+  const bool active = stripe < stripes;
+  const int h_item = item / (D / 4), c_item = 4 * (item % (D / 4));
+  const __amdgpu_buffer_rsrc_t po = buffer(a.part_o + head0 * a.nsplit * D,
+                                           (uint32_t)(G * a.nsplit * D * 4));
+  // loads of splits stripe + stripes * (j0 + j); out of range: an offset past
+  // the resource, which reads 0 without touching memory
+  auto load_batch = [&](f32x4 (&v)[kBatch], int j0) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int s = stripe + stripes * (j0 + j);
+      const uint32_t off = (active && s < nact)
+                               ? (uint32_t)(((h_item * a.nsplit + s) * D + c_item) * 4)
+                               : 0x80000000u;
+      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(po, off, 0, kCoherent));
+    }
+  };
+  f32x4 first[kBatch];
+  load_batch(first, 0);
+  const int N = (T + kBlockTokens - 1) / kBlockTokens;
+  float mass0[kMaxGroup];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+    mass0[h] = (a.stats != nullptr && h < G && (int)threadIdx.x < N)
+                   ? load_agent(a.stats + (head0 + h) * a.max_blocks + threadIdx.x)
+                   : 0.f;
 
   // per head: global max / sum and the per-split rescale factors
   for (int h = w; h < G; h += kWaves) {
@@ -376,35 +474,33 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
   }
   __syncthreads();
 
-  // out: thread -> (head, 4 columns, stripe of splits); stripes summed in LDS
-  const int items = G * (D / 4);
-  const int stripes = items >= kThreads ? 1 : kThreads / items;
-  const __amdgpu_buffer_rsrc_t po = buffer(a.part_o + head0 * a.nsplit * D,
-                                           (uint32_t)(G * a.nsplit * D * 4));
-  for (int base = 0; base < items; base += kThreads) {
-    const int item = base + threadIdx.x % (items >= kThreads ? kThreads : items);
-    const int stripe = items >= kThreads ? 0 : threadIdx.x / items;
-    const int h = item / (D / 4), c = 4 * (item % (D / 4));
+  {
+    const int per_stripe = (nact - stripe + stripes - 1) / stripes;  // splits of this stripe
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (item < items && stripe < stripes) {
-#pragma unroll 16
-      for (int s = stripe; s < nact; s += stripes)
-        acc += sm.f[h][s] * __builtin_bit_cast(
-                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           po, (uint32_t)(((h * a.nsplit + s) * D + c) * 4), 0,
-                                           kCoherent));
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int s = stripe + stripes * j;
+      if (active && s < nact) acc += sm.f[h_item][s] * first[j];
+    }
+    for (int j0 = kBatch; j0 < per_stripe; j0 += kBatch) {
+      f32x4 v[kBatch];
+      load_batch(v, j0);
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int s = stripe + stripes * (j0 + j);
+        if (active && s < nact) acc += sm.f[h_item][s] * v[j];
+      }
     }
     if (stripes > 1) {
       sm.red[threadIdx.x] = acc;
       __syncthreads();
-      if (threadIdx.x < items) {
+      if (threadIdx.x < items)
         for (int st = 1; st < stripes; ++st) acc += sm.red[st * items + threadIdx.x];
-      }
     }
-    if (threadIdx.x < (items >= kThreads ? kThreads : items) && item < items) {
-      const float L = sm.L[h];
+    if ((int)threadIdx.x < items) {
+      const float L = sm.L[h_item];
       const f32x4 o = L > 0.f ? acc * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4 *>(a.out + (head0 + h) * D + c) = o;
+      *reinterpret_cast<f32x4 *>(a.out + (head0 + h_item) * D + c_item) = o;
     }
   }
   if (a.lse != nullptr && threadIdx.x < G) {
@@ -420,15 +516,18 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
 
   // block score: sum over the group's heads of the softmax mass of the block
   // (mass stored relative to its split's max; f brings it to the head's max)
-  const int N = (T + kBlockTokens - 1) / kBlockTokens;
   const int blocks_per_split = a.chunks_per_wg / kChunksPerBlock;
   for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
     float score = 0.f;
     if (n < N) {
       const int s = n / blocks_per_split;
-      for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h >= G) continue;
+        const float mass = n < kThreads ? mass0[h]
+                                        : load_agent(a.stats + (head0 + h) * a.max_blocks + n);
         const float L = sm.L[h];
-        if (L > 0.f) score += load_agent(a.stats + (head0 + h) * a.max_blocks + n) * sm.f[h][s] / L;
+        if (L > 0.f) score += mass * sm.f[h][s] / L;
       }
       sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
     }
@@ -437,7 +536,7 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
   }
   if (a.idx_out != nullptr) {
     __syncthreads();
-    select_topk(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
+    if (w == 0) select_topk_wave(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
   }
 }
 
@@ -808,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void score_topk(TopkArgs a) {
     sm.keys[n] = sc > 0.f ? __float_as_uint(sc) : 0u;
   }
   __syncthreads();
-  select_topk(sm, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k);
+  if (threadIdx.x < 64) select_topk_wave(sm, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k);
 }
 
 // Kernel timers: event pairs recorded around launches while running.
