@@ -182,7 +182,11 @@ def main():
         _, kern_f = timed(full.run, args.steps, args.warmup, torch,
                           (hylra.KERNEL_FULL_ATTN,), hylra)
         ms_f, _ = graph_timed(full.run, args.steps, args.warmup, torch)
-        allreset = hylra.PolicyPlan(layers, list(range(L)), k)
+        # every layer resets and computes its top-k (the index log makes the
+        # library keep scores and selection on layers no one reuses)
+        allreset = hylra.PolicyPlan(
+            layers, list(range(L)), k,
+            idx_log=torch.empty(L, wl.batch, wl.num_kv_heads, k, dtype=torch.int32, device="cuda"))
         ms_a, _ = graph_timed(allreset.run, args.steps, args.warmup, torch)
         result_extra.update({
             "full_steps_per_s": 1000.0 / ms_f,

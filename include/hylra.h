@@ -122,7 +122,9 @@ hylra_status hylra_decode_sparse(const hylra_shape *shape, const void *q, const 
  * otherwise).  q, kv, out and lse are host arrays of num_layers entries (lse
  * may be NULL, or hold NULL entries).  idx_log (device, nullable)
  * [num_layers][B][Hkv][k] receives the index set each layer computed or
- * reused.  Everything is enqueued on one stream with no host synchronisation. */
+ * reused.  With idx_log NULL, a reset layer whose indices the next layer does
+ * not reuse skips the block scores and top-k (nothing would read them).
+ * Everything is enqueued on one stream with no host synchronisation. */
 hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, const int32_t *src,
                               int32_t k, const void *const *q, const hylra_kv *kv,
                               float *const *out, float *const *lse, int32_t *idx_log,

@@ -11,6 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhylra.so")
 SOURCES = ["hylra_kernels.hip", "hylra_api.cpp"]
 ARCH = os.environ.get("HYLRA_OFFLOAD_ARCH", "gfx950")
+COMPILE_TIMEOUT_S = 900  # a stuck compiler fails the build instead of hanging it
 
 # Packed-fp32 VALU forms are disabled for every device compile.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -38,13 +39,13 @@ def build(verbose: bool = False) -> str:
         cmd += [path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        subprocess.check_call(cmd, timeout=COMPILE_TIMEOUT_S)
         objs.append(obj)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+    subprocess.check_call(cmd, timeout=COMPILE_TIMEOUT_S)
     os.replace(tmp, LIB)
     for obj in objs:
         os.remove(obj)

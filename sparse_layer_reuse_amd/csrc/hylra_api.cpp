@@ -315,7 +315,10 @@ hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, cons
     float *lj = lse ? lse[j] : nullptr;
     hylra_status st;
     if (src[j] == j) {
-      int32_t *dst = idx_log ? idx_log + (size_t)j * row : w.idx;
+      // the index set of a reset layer is needed only if the next layer
+      // reuses it, or the caller logs it
+      const bool used = idx_log != nullptr || (j + 1 < num_layers && src[j + 1] == j);
+      int32_t *dst = used ? (idx_log ? idx_log + (size_t)j * row : w.idx) : nullptr;
       st = run_full(shape, q[j], &kv[j], out[j], lj, nullptr, dst, k, w, hip_stream);
     } else {
       const int32_t *carried = idx_log ? idx_log + (size_t)src[j] * row : w.idx;

@@ -223,6 +223,7 @@ struct EpiSmem {
   float f[kMaxGroup][kMaxSplits];  // per (head, split) rescale factor 2^(m_s - M)
   float M[kMaxGroup];
   float L[kMaxGroup];
+  float invL[kMaxGroup];
   f32x4 red[kThreads];
   uint32_t keys[kMaxBlocks];
   int hist[256];
@@ -470,10 +471,12 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
     if (lane == 0) {
       sm.M[h] = M;
       sm.L[h] = L;
+      sm.invL[h] = L > 0.f ? 1.f / L : 0.f;
     }
   }
   __syncthreads();
 
+  f32x4 out_v = {0.f, 0.f, 0.f, 0.f};
   {
     const int per_stripe = (nact - stripe + stripes - 1) / stripes;  // splits of this stripe
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -497,26 +500,34 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
       if (threadIdx.x < items)
         for (int st = 1; st < stripes; ++st) acc += sm.red[st * items + threadIdx.x];
     }
+    out_v = acc;
+  }
+  // every global store of the epilogue comes after its last barrier, so no
+  // barrier waits for stores to complete
+  auto store_outputs = [&]() {
     if ((int)threadIdx.x < items) {
       const float L = sm.L[h_item];
-      const f32x4 o = L > 0.f ? acc * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 o = L > 0.f ? out_v * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f32x4 *>(a.out + (head0 + h_item) * D + c_item) = o;
     }
+    if (a.lse != nullptr && threadIdx.x < G) {
+      const float L = sm.L[threadIdx.x];
+      a.lse[head0 + threadIdx.x] = L > 0.f ? (sm.M[threadIdx.x] + __log2f(L)) * kLn2 : kNegInf;
+    }
+    if (a.sel_log != nullptr) {
+      const int64_t r0 = ((int64_t)b * a.num_kv_heads + g) * a.k;
+      for (int r = threadIdx.x; r < a.k; r += kThreads) a.sel_log[r0 + r] = a.sel[r0 + r];
+    }
+  };
+  if (a.stats == nullptr) {
+    store_outputs();
+    return;
   }
-  if (a.lse != nullptr && threadIdx.x < G) {
-    const float L = sm.L[threadIdx.x];
-    a.lse[head0 + threadIdx.x] = L > 0.f ? (sm.M[threadIdx.x] + __log2f(L)) * kLn2 : kNegInf;
-  }
-
-  if (a.sel_log != nullptr) {
-    const int64_t r0 = ((int64_t)b * a.num_kv_heads + g) * a.k;
-    for (int r = threadIdx.x; r < a.k; r += kThreads) a.sel_log[r0 + r] = a.sel[r0 + r];
-  }
-  if (a.stats == nullptr) return;
 
   // block score: sum over the group's heads of the softmax mass of the block
   // (mass stored relative to its split's max; f brings it to the head's max)
   const int blocks_per_split = a.chunks_per_wg / kChunksPerBlock;
+  float score0 = 0.f;  // score of block n = thread, stored after the barrier
   for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
     float score = 0.f;
     if (n < N) {
@@ -526,18 +537,22 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
         if (h >= G) continue;
         const float mass = n < kThreads ? mass0[h]
                                         : load_agent(a.stats + (head0 + h) * a.max_blocks + n);
-        const float L = sm.L[h];
-        if (L > 0.f) score += mass * sm.f[h][s] / L;
+        score += mass * sm.f[h][s] * sm.invL[h];
       }
       sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
     }
-    if (a.score_out != nullptr)
+    if (n < kThreads) {
+      score0 = score;
+    } else if (a.score_out != nullptr) {
       a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = score;
+    }
   }
-  if (a.idx_out != nullptr) {
-    __syncthreads();
-    if (w == 0) select_topk_wave(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
-  }
+  __syncthreads();
+  if (a.idx_out != nullptr && w == 0)
+    select_topk_wave(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
+  if (a.score_out != nullptr && (int)threadIdx.x < a.max_blocks)
+    a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + threadIdx.x] = score0;
+  store_outputs();
 }
 
 // Common prologue: range of the workgroup, early exits.  Returns false if the
