@@ -12,8 +12,11 @@ scores + top-k).
 Prints one JSON line.  `value` is hybrid decode steps/s.  `roofline` covers
 the dominant kernel (full split attention of the reset layers): algorithmic
 bytes per launch = 4*B*Hkv*T*d (bf16 K and V, each read once), divided by its
-average launch time from HIP events recorded on the launch stream during the
-timed hybrid steps.  `cpu_baseline` times the CPU oracle on the host.
+average launch time from HIP events that each launch stamps itself on its
+stream (hipExtLaunchKernel) during the timed eager hybrid steps; `traffic` is
+the HBM bytes per launch from the committed rocprofv3 counter summary, null
+once the kernel source differs from the one profiled.  `cpu_baseline` times
+the CPU oracle on the host.
 """
 from __future__ import annotations
 
@@ -44,7 +47,41 @@ def parse():
                    help="budget of the CPU oracle baseline (0 disables it)")
     p.add_argument("--skip-baselines", action="store_true",
                    help="time only the hybrid step (for short profiler runs)")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only copy a MIB-sized buffer 4 times (calibrates HBM byte counters)")
     return p.parse_args()
+
+
+def copy_probe(mib):
+    """Four device-to-device copies of `mib` MiB: a kernel of known traffic
+    (mib MiB read + mib MiB written each) for scaling profiler byte counters."""
+    import torch
+    x = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(4):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": mib << 20, "copies": 4}), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per full-attention launch from the committed rocprofv3 PMC
+    summary of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a copy
+    kernel of known size), or None when there is none or when the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_traffic_%s.json" % workload)
+    src = os.path.join(ROOT, "sparse_layer_reuse_amd", "csrc", "hylra_kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != digest or rec.get("workload") != workload:
+        return None
+    return rec.get("full_layer_traffic_bytes")
 
 
 def policy_for(wl, hylra, theta, L):
@@ -110,42 +147,53 @@ def graph_timed(fn, steps, warmup, torch):
 
 
 def cpu_baseline(wl, layers, src, k, budget_s):
-    """Oracle timed on the host over a prefix of the step's layers; the step
-    time is extrapolated from the mean reset-layer and reuse-layer times."""
+    """Oracle timed on the host: passes over the step's layers in order (the
+    carried indices flow from each reset layer to its reuse layers) until the
+    time budget is spent; the step time is the mean reset-layer time times
+    the number of reset layers plus the mean reuse-layer time times the
+    number of reuse layers."""
     import oracle
     from sparse_layer_reuse_amd import synth
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
     t_reset, t_reuse = [], []
     carried = None
+    passes, measured = 0, 0
     t_start = time.time()
-    for j, lay in enumerate(layers):
-        o = synth.layer_to_oracle(lay)
-        t0 = time.perf_counter()
-        if src[j] == j:
-            _, _, score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
-                                             o["ctx"], num_kv_heads=wl.num_kv_heads)
-            carried, _ = oracle.topk(score, o["ctx"], k)
-            t_reset.append(time.perf_counter() - t0)
+    done = False
+    while not done:
+        for j, lay in enumerate(layers):
+            o = synth.layer_to_oracle(lay)
+            t0 = time.perf_counter()
+            if src[j] == j:
+                _, _, score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
+                                                 o["ctx"], num_kv_heads=wl.num_kv_heads)
+                carried, _ = oracle.topk(score, o["ctx"], k)
+                t_reset.append(time.perf_counter() - t0)
+            else:
+                oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
+                              num_kv_heads=wl.num_kv_heads, sel=carried, k=k)
+                t_reuse.append(time.perf_counter() - t0)
+            del o
+            measured += 1
+            if time.time() - t_start > budget_s and t_reset and (t_reuse or j + 1 == len(layers)):
+                done = True
+                break
         else:
-            oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
-                          num_kv_heads=wl.num_kv_heads, sel=carried, k=k)
-            t_reuse.append(time.perf_counter() - t0)
-        del o
-        if time.time() - t_start > budget_s and t_reset and (t_reuse or j + 1 == len(layers)):
-            break
+            passes += 1
     n_reset = sum(1 for j, s in enumerate(src) if s == j)
     n_reuse = len(src) - n_reset
     mean = lambda v: sum(v) / len(v) if v else 0.0
     step_s = n_reset * mean(t_reset) + n_reuse * mean(t_reuse)
-    measured = len(t_reset) + len(t_reuse)
     return {
         "value": 1.0 / step_s if step_s > 0 else None,
         "unit": "steps/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "layers 0-%d of the hybrid step (%d reset, %d reuse) timed, step time "
-                  "extrapolated to %d reset + %d reuse layers; float64 C oracle, OpenMP"
-                  % (measured - 1, len(t_reset), len(t_reuse), n_reset, n_reuse),
+        "sample": "%d layer calls timed (%d full passes over the %d-layer hybrid step, then "
+                  "layers 0-%d): %d reset, %d reuse; step time = %d x mean reset-layer time "
+                  "+ %d x mean reuse-layer time; float64 C oracle, OpenMP, %.1f s"
+                  % (measured, passes, len(layers), (measured - 1) % len(layers),
+                     len(t_reset), len(t_reuse), n_reset, n_reuse, time.time() - t_start),
         "reset_layer_s": mean(t_reset),
         "reuse_layer_s": mean(t_reuse),
     }
@@ -153,6 +201,9 @@ def cpu_baseline(wl, layers, src, k, budget_s):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -237,7 +288,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "bytes_per_launch": full_bytes,
             "avg_launch_us": full_us,
         },

@@ -145,8 +145,11 @@ hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
                              double *sim_sum);
 
 /* Kernel timer (instrumentation).  While the timer of a kernel kind runs,
- * every launch of that kind is bracketed by a pair of HIP events recorded on
- * the launch stream (the first `capacity` launches).  hylra_timer_stop waits
+ * every launch of that kind (the first `capacity` launches) carries a pair
+ * of HIP events that the dispatch itself stamps at its start and end
+ * (hipExtLaunchKernel), so the time is the kernel's own execution on the
+ * launch stream.  Timers must not run while the stream is being captured
+ * into a graph.  hylra_timer_stop waits
  * for the recorded events and returns the summed kernel time in milliseconds
  * and the number of timed launches (both pointers nullable).  Timers are
  * process-global and not thread-safe; starting a running timer restarts it. */

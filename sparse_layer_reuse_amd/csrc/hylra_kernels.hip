@@ -5,10 +5,10 @@
 // extraction; reuse layers: attention over the carried KV subset) and 2.4
 // (selection over fixed 128-token blocks).
 //
-// One launch per layer.  Grid (nsplit, Hkv, B), 256 threads (4 wavefronts).
+// One launch per layer.  Grid (nsplit, Hkv, B), 512 threads (8 wavefronts).
 //   split pass   each wavefront consumes 32-token chunks of its workgroup's
 //                range, keeping an online-softmax state for the G query heads
-//                of the KV head; the four states are merged in LDS and written
+//                of the KV head; the eight states are merged in LDS and written
 //                as the workgroup's partial.  bf16 K/V: q.K and p.V on MFMA
 //                (v_mfma_f32_16x16x32_bf16); float32 K/V: vector ALU.
 //                Full mode walks every chunk of the sequence, a wavefront
@@ -23,6 +23,7 @@
 // A separate small kernel selects the top-k of a caller-given score array.
 //
 // Softmax state is kept in base 2: x = s * scale * log2(e), p = 2^(x - m).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -112,7 +113,7 @@ __device__ __forceinline__ bool resolve_chunk(const AttnArgs &a, int b, int g, i
 }
 
 // The i-th chunk position of wavefront w in a workgroup range starting at
-// c_begin.  Full mode (blocked): wavefront w takes whole blocks w, w+4, ...
+// c_begin.  Full mode (blocked): wavefront w takes whole blocks w, w+8, ...
 // Sparse mode: chunks are dealt round-robin.
 __device__ __forceinline__ int chunk_of(bool blocked, int c_begin, int w, int i) {
   return blocked ? c_begin + kChunksPerBlock * (w + kWaves * (i / kChunksPerBlock)) +
@@ -341,7 +342,7 @@ __device__ void write_empty(const AttnArgs &a, int b, int g, int D) {
     }
 }
 
-// Writes the workgroup partial from the four wavefront states (and, in full
+// Writes the workgroup partial from the eight wavefront states (and, in full
 // mode with scores, the block masses rescaled to the partial's max), then
 // counts the workgroup's arrival.  Returns true in the last of the nact
 // workgroups of (b, g), which then runs the epilogue.
@@ -925,7 +926,10 @@ __global__ __launch_bounds__(kThreads) void score_topk(TopkArgs a) {
   if (threadIdx.x < 64) select_topk_wave(sm, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k);
 }
 
-// Kernel timers: event pairs recorded around launches while running.
+// Kernel timers: while a timer runs, each launch of its kind takes an event
+// pair that the launch itself records (hipExtLaunchKernel stamps the events
+// with the dispatch's own start and end), so the elapsed time is the kernel's
+// execution without the separate event packets' overhead.
 struct KernelTimer {
   bool running = false;
   int recorded = 0;
@@ -934,15 +938,14 @@ struct KernelTimer {
 KernelTimer g_timers[kNumTimers];
 
 struct TimerScope {
-  KernelTimer *t;
-  hipStream_t st;
-  bool on;
-  TimerScope(int kind, hipStream_t s) : t(&g_timers[kind]), st(s) {
-    on = t->running && t->recorded < (int)t->start.size();
-    if (on) (void)hipEventRecord(t->start[t->recorded], st);
-  }
-  ~TimerScope() {
-    if (on) (void)hipEventRecord(t->stop[t->recorded++], st);
+  hipEvent_t start = nullptr, stop = nullptr;
+  explicit TimerScope(int kind) {
+    KernelTimer &t = g_timers[kind];
+    if (t.running && t.recorded < (int)t.start.size()) {
+      start = t.start[t.recorded];
+      stop = t.stop[t.recorded];
+      ++t.recorded;
+    }
   }
 };
 
@@ -989,21 +992,26 @@ int timer_stop(int kind, double *total_ms, int *launches) {
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream) {
   const dim3 grid(a.nsplit, a.num_kv_heads, batch);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  TimerScope timer(a.sel == nullptr ? kTimerFullAttn : kTimerSparseAttn, st);
+  const TimerScope tm(a.sel == nullptr ? kTimerFullAttn : kTimerSparseAttn);
+  const dim3 block(kThreads);
   if (dtype == 1) {
-    if (head_dim == 128) hipLaunchKernelGGL(attn_split_bf16<128>, grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL(attn_split_bf16<64>, grid, dim3(kThreads), 0, st, a);
+    if (head_dim == 128)
+      hipExtLaunchKernelGGL(attn_split_bf16<128>, grid, block, 0, st, tm.start, tm.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(attn_split_bf16<64>, grid, block, 0, st, tm.start, tm.stop, 0, a);
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL(attn_split_f32<128>, grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL(attn_split_f32<64>, grid, dim3(kThreads), 0, st, a);
+    if (head_dim == 128)
+      hipExtLaunchKernelGGL(attn_split_f32<128>, grid, block, 0, st, tm.start, tm.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(attn_split_f32<64>, grid, block, 0, st, tm.start, tm.stop, 0, a);
   }
   return (int)hipGetLastError();
 }
 
 int launch_topk(const TopkArgs &a, int batch, void *stream) {
-  TimerScope timer(kTimerTopk, static_cast<hipStream_t>(stream));
-  hipLaunchKernelGGL(score_topk, dim3(a.num_kv_heads, batch), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+  const TimerScope tm(kTimerTopk);
+  hipExtLaunchKernelGGL(score_topk, dim3(a.num_kv_heads, batch), dim3(kThreads), 0,
+                        static_cast<hipStream_t>(stream), tm.start, tm.stop, 0, a);
   return (int)hipGetLastError();
 }
 
