@@ -21,7 +21,8 @@
  *   - Layouts (row-major, innermost last):
  *       q            [B][Hq][d]
  *       K pool       [num_pages][Hkv][128][d]   token-major page tile
- *       V pool       [num_pages][Hkv][d][128]   dimension-major page tile
+ *       V pool       [num_pages][Hkv][4][d][32] a page as four 32-token
+ *                                               sub-tiles, each dimension-major
  *       block_table  [B][max_blocks_per_seq] int32, logical block -> page
  *       ctx_lens     [B] int32, tokens of each sequence (device memory)
  *       out          [B][Hq][d] float32, lse [B][Hq] float32 (natural log)
@@ -72,7 +73,7 @@ typedef struct {
 
 typedef struct {
   const void *k_pool;         /* [num_pages][Hkv][128][d] */
-  const void *v_pool;         /* [num_pages][Hkv][d][128] */
+  const void *v_pool;         /* [num_pages][Hkv][4][d][32] */
   int64_t num_pages;          /* >= 1 */
   const int32_t *block_table; /* [B][max_blocks_per_seq] */
   const int32_t *ctx_lens;    /* [B] */

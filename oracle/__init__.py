@@ -10,8 +10,8 @@ brute-force check are plain Python below.
 
 Array conventions (numpy): float32 arrays are fp32 data, uint16 arrays are
 bfloat16 bit patterns.  K pages are ``[pages][Hkv][128][d]``, V pages are
-``[pages][Hkv][d][128]``; ``table`` is ``[B][max_blocks]`` int32 and ``ctx``
-``[B]`` int32.
+``[pages][Hkv][4][d][32]`` (four 32-token sub-tiles, each dimension-major);
+``table`` is ``[B][max_blocks]`` int32 and ``ctx`` ``[B]`` int32.
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 library routines, closed forms, brute force or hand-derived fixtures.
@@ -27,6 +27,7 @@ import subprocess
 import numpy as np
 
 BLOCK = 128
+SUB = 32  # tokens per V sub-tile
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hylra_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -105,8 +106,8 @@ def attend(q, k_pool, v_pool, table, ctx, *, num_kv_heads, scale=None, sel=None,
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     pages = k_pool.shape[0]
-    if k_pool.shape != (pages, Hkv, BLOCK, d) or v_pool.shape != (pages, Hkv, d, BLOCK):
-        raise ValueError("K pool must be [pages][Hkv][128][d], V pool [pages][Hkv][d][128]")
+    if k_pool.shape != (pages, Hkv, BLOCK, d) or v_pool.shape != (pages, Hkv, BLOCK // SUB, d, SUB):
+        raise ValueError("K pool must be [pages][Hkv][128][d], V pool [pages][Hkv][4][d][32]")
     max_blocks = table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)

@@ -23,7 +23,8 @@
  * Memory layout read here (the same bits the GPU path reads):
  *   q      [B][Hq][d]                      element type `dtype`
  *   K pool [pages][Hkv][128][d]            token-major page tile
- *   V pool [pages][Hkv][d][128]            dimension-major page tile
+ *   V pool [pages][Hkv][4][d][32]          a page as four 32-token sub-tiles,
+ *                                          each dimension-major
  *   table  [B][max_blocks]                 logical block -> physical page
  *   ctx    [B]                             context length T_b in tokens
  * dtype 0 = IEEE float32, 1 = bfloat16 (upper 16 bits of a float32).
@@ -39,6 +40,7 @@
 #include <string.h>
 
 #define ORACLE_BLOCK 128
+#define ORACLE_SUBTILE 32
 
 /* One element of a q / K / V buffer as an exact double. */
 static double elem(const void *base, int64_t i, int dtype) {
@@ -54,7 +56,9 @@ static int64_t k_index(int64_t page, int Hkv, int g, int tok, int d, int c) {
 }
 
 static int64_t v_index(int64_t page, int Hkv, int g, int tok, int d, int c) {
-  return ((page * Hkv + g) * d + c) * ORACLE_BLOCK + tok;
+  const int64_t sub = tok / ORACLE_SUBTILE;
+  return (((page * Hkv + g) * (ORACLE_BLOCK / ORACLE_SUBTILE) + sub) * d + c) * ORACLE_SUBTILE +
+         tok % ORACLE_SUBTILE;
 }
 
 static int clamp_ctx(int t, int max_blocks) {

@@ -201,10 +201,11 @@ hylra_status run_sparse(const hylra_shape *s, const void *q, const hylra_kv *kv,
 namespace hylra {
 
 // Split plans: about 256 workgroups per launch (one 8-wavefront workgroup
-// resident per compute unit on a 256-CU part).  Full mode: a multiple of
-// 4 * 8 chunks per workgroup, so every wavefront takes whole 128-token blocks;
-// sparse mode: a multiple of 8 chunks.  At most kMaxSplits workgroups per
-// (sequence, KV head) and kMaxWgChunks chunks per workgroup.
+// resident per compute unit on a 256-CU part), each taking a multiple of 8
+// chunks (one per wavefront; in full mode also whole 128-token blocks, so a
+// block's mass never straddles two workgroups).  At most kMaxSplits workgroups
+// per (sequence, KV head) and kMaxWgChunks chunks per workgroup.
+static_assert(kWavesPerGroup % kChunksPerBlock == 0, "a workgroup unit must hold whole blocks");
 constexpr long kTargetWorkgroups = 256;
 
 static SplitPlan make_plan(long chunks_per_seq, long rows, long unit) {
@@ -221,7 +222,7 @@ static SplitPlan make_plan(long chunks_per_seq, long rows, long unit) {
 
 SplitPlan plan_full(int batch, int num_kv_heads, int max_blocks) {
   return make_plan((long)kChunksPerBlock * max_blocks, (long)batch * num_kv_heads,
-                   (long)kChunksPerBlock * kWavesPerGroup);
+                   (long)kWavesPerGroup);
 }
 
 SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k) {

@@ -11,10 +11,12 @@
 //                of the KV head; the eight states are merged in LDS and written
 //                as the workgroup's partial.  bf16 K/V: q.K and p.V on MFMA
 //                (v_mfma_f32_16x16x32_bf16); float32 K/V: vector ALU.
-//                Full mode walks every chunk of the sequence, a wavefront
-//                taking whole 128-token blocks so it can also sum each block's
-//                softmax mass; sparse mode walks the chunks of the selected
-//                blocks through the block table.
+//                Full mode walks every chunk of the sequence, sparse mode the
+//                chunks of the selected blocks through the block table.  The
+//                chunks are dealt round-robin (wavefront w takes w, w+8, ...),
+//                so the eight wavefronts stream neighbouring chunks together.
+//                Full mode records each chunk's softmax mass; a block's four
+//                chunk masses are summed when the partial is written.
 //   epilogue     the last workgroup of a (sequence, KV head) to finish (device
 //                scope arrival counter; partials handed over with coherent
 //                device-scope stores and loads) merges them into out / lse and,
@@ -40,7 +42,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kWavesPerGroup;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxWgBlocks = kMaxWgChunks / kChunksPerBlock;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 (raw 32-bit data) on gfx9
@@ -113,18 +114,13 @@ __device__ __forceinline__ bool resolve_chunk(const AttnArgs &a, int b, int g, i
 }
 
 // The i-th chunk position of wavefront w in a workgroup range starting at
-// c_begin.  Full mode (blocked): wavefront w takes whole blocks w, w+8, ...
-// Sparse mode: chunks are dealt round-robin.
-__device__ __forceinline__ int chunk_of(bool blocked, int c_begin, int w, int i) {
-  return blocked ? c_begin + kChunksPerBlock * (w + kWaves * (i / kChunksPerBlock)) +
-                       i % kChunksPerBlock
-                 : c_begin + w + kWaves * i;
+// c_begin: chunks are dealt round-robin, so at any time the wavefronts of a
+// workgroup read neighbouring chunks (the four chunks of a block together).
+__device__ __forceinline__ int chunk_of(int c_begin, int w, int i) {
+  return c_begin + w + kWaves * i;
 }
-// Whether the i-th chunk of wavefront w still belongs to the range (for the
-// blocked order: whether its block starts inside the range).
-__device__ __forceinline__ bool chunk_live(bool blocked, int c_begin, int c_end, int w, int i) {
-  return blocked ? c_begin + kChunksPerBlock * (w + kWaves * (i / kChunksPerBlock)) < c_end
-                 : c_begin + w + kWaves * i < c_end;
+__device__ __forceinline__ bool chunk_live(int c_begin, int c_end, int w, int i) {
+  return chunk_of(c_begin, w, i) < c_end;
 }
 
 // Wavefront reductions on DPP lane permutes (quad perms, row mirrors, row
@@ -209,14 +205,14 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-// LDS of the split pass: the wavefront states and the block masses.
+// LDS of the split pass: the wavefront states and the chunk masses.
 template <int D>
 struct SplitSmem {
   float m[kWaves][kMaxGroup];
   float l[kWaves][kMaxGroup];
   float o[kWaves][kMaxGroup][D];
-  float bm[kMaxWgBlocks][kMaxGroup];  // block: running max when its mass was taken
-  float bp[kMaxWgBlocks][kMaxGroup];  // block: softmax mass relative to bm
+  float cm[kMaxWgChunks][kMaxGroup];  // chunk: running max after the chunk
+  float cp[kMaxWgChunks][kMaxGroup];  // chunk: its softmax mass relative to cm
 };
 
 // LDS used by the epilogue and the top-k selection.
@@ -384,7 +380,13 @@ __device__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact, i
       float m = kNegInf;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm.m[w][h]);
-      const float v = m == kNegInf ? 0.f : sm.bp[nl][h] * rescale(sm.bm[nl][h], m);
+      float v = 0.f;
+      if (m != kNegInf)
+#pragma unroll
+        for (int j = 0; j < kChunksPerBlock; ++j) {
+          const int cl = kChunksPerBlock * nl + j;  // chunk of the block, relative to c_begin
+          if (c_begin + cl < c_end) v += sm.cp[cl][h] * rescale(sm.cm[cl][h], m);
+        }
       if (nb0 + nl < N) store_agent(a.stats + (head0 + h) * a.max_blocks + nb0 + nl, v);
     }
   }
@@ -604,19 +606,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   Range r;
   if (!wg_range(a, s, g, b, D, r)) return;
   const int T = r.T, c_begin = r.c_begin, c_end = r.c_end;
-  const bool blocked = a.sel == nullptr;
   const bool want_mass = a.stats != nullptr;
 
   const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int quad = lane >> 4, m16 = lane & 15;
   const int G = a.group;
-
-  if (want_mass)
-    for (int i = threadIdx.x; i < kMaxWgBlocks * kMaxGroup; i += kThreads) {
-      sm.split.bm[i / kMaxGroup][i % kMaxGroup] = kNegInf;
-      sm.split.bp[i / kMaxGroup][i % kMaxGroup] = 0.f;
-    }
-  __syncthreads();
 
   bf16x8 qop[D / 32];
   {
@@ -630,7 +624,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
 
-  float m_run = kNegInf, l_run = 0.f, bmass = 0.f;
+  float m_run = kNegInf, l_run = 0.f, cmass = 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -640,7 +634,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int Hkv = a.num_kv_heads;
   // per-lane byte offsets inside a chunk's K rows / V columns (chunk-invariant)
   const uint32_t k_lane = (uint32_t)(((8 * (m16 >> 2) + (m16 & 3)) * D + 8 * quad) * 2);
-  const uint32_t v_lane = (uint32_t)((m16 * kBlockTokens + 8 * quad) * 2);
+  const uint32_t v_lane = (uint32_t)((m16 * kChunkTokens + 8 * quad) * 2);
 
   // Issues the 16-byte loads of chunk `pos` into t through buffer resources
   // spanning just that chunk; returns its valid token count.  A position past
@@ -656,11 +650,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       valid = 0;
     }
     const int64_t tile = (int64_t)page * Hkv + g;
+    // K chunk: 32 token rows of d; V sub-tile: d rows of 32 tokens (8 KiB each at d = 128)
     const char *kb = kpool + (tile * kBlockTokens + sub * kChunkTokens) * D * 2;
-    const char *vb = vpool + (tile * D * kBlockTokens + sub * kChunkTokens) * 2;
+    const char *vb = vpool + (tile * kChunksPerBlock + sub) * D * kChunkTokens * 2;
     const __amdgpu_buffer_rsrc_t krs = buffer(kb, ok ? kChunkTokens * D * 2 : 0);
-    const __amdgpu_buffer_rsrc_t vrs =
-        buffer(vb, ok ? (D - 1) * kBlockTokens * 2 + kChunkTokens * 2 : 0);
+    const __amdgpu_buffer_rsrc_t vrs = buffer(vb, ok ? kChunkTokens * D * 2 : 0);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -668,7 +662,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         t.k[h][k] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane, (4 * h * D + 32 * k) * 2, 0);
 #pragma unroll
     for (int n = 0; n < D / 16; ++n)
-      t.v[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_lane, n * 16 * kBlockTokens * 2, 0);
+      t.v[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_lane, n * 16 * kChunkTokens * 2, 0);
     return valid;
   };
 
@@ -708,7 +702,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
-    bmass = bmass * alpha + ps;
+    cmass = ps;
     m_run = m_new;
     float al[4];
 #pragma unroll
@@ -731,15 +725,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  // block-mass bookkeeping of the i-th chunk (full mode with scores): the
-  // mass restarts with each block and is recorded after every chunk.
+  // consumes the i-th chunk of the wavefront and, in full mode with scores,
+  // records its softmax mass (0 for a chunk without tokens)
   auto step = [&](const BfTile<D> &t, int i, int valid) {
-    if (want_mass && i % kChunksPerBlock == 0) bmass = 0.f;
+    cmass = 0.f;
     if (valid > 0) consume(t, valid);
     if (want_mass && quad == 0 && m16 < G) {
-      const int nl = w + kWaves * (i / kChunksPerBlock);
-      sm.split.bm[nl][m16] = m_run;
-      sm.split.bp[nl][m16] = bmass;
+      const int cl = w + kWaves * i;
+      sm.split.cm[cl][m16] = m_run;
+      sm.split.cp[cl][m16] = cmass;
     }
   };
 
@@ -747,16 +741,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // current one is consumed.
   BfTile<D> ta, tb;
   int i = 0;
-  bool live = chunk_live(blocked, c_begin, c_end, w, 0);
-  int va = issue(ta, chunk_of(blocked, c_begin, w, 0), live);
+  bool live = chunk_live(c_begin, c_end, w, 0);
+  int va = issue(ta, chunk_of(c_begin, w, 0), live);
   while (live) {
-    const bool live_b = chunk_live(blocked, c_begin, c_end, w, i + 1);
-    const int vb = issue(tb, chunk_of(blocked, c_begin, w, i + 1), live_b);
+    const bool live_b = chunk_live(c_begin, c_end, w, i + 1);
+    const int vb = issue(tb, chunk_of(c_begin, w, i + 1), live_b);
     step(ta, i, va);
     ++i;
     if (!live_b) break;
-    const bool live_a = chunk_live(blocked, c_begin, c_end, w, i + 1);
-    va = issue(ta, chunk_of(blocked, c_begin, w, i + 1), live_a);
+    const bool live_a = chunk_live(c_begin, c_end, w, i + 1);
+    va = issue(ta, chunk_of(c_begin, w, i + 1), live_a);
     step(tb, i, vb);
     ++i;
     live = live_a;
@@ -789,18 +783,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   Range r;
   if (!wg_range(a, s, g, b, D, r)) return;
   const int T = r.T, c_begin = r.c_begin, c_end = r.c_end;
-  const bool blocked = a.sel == nullptr;
   const bool want_mass = a.stats != nullptr;
 
   constexpr int CPL = D / 64;  // output columns per lane
   const int G = a.group;
   const float *qg = static_cast<const float *>(a.q) + ((int64_t)b * a.num_q_heads + g * G) * D;
   for (int i = threadIdx.x; i < G * D; i += kThreads) q_s[i / D][i % D] = qg[i];
-  if (want_mass)
-    for (int i = threadIdx.x; i < kMaxWgBlocks * kMaxGroup; i += kThreads) {
-      sm.split.bm[i / kMaxGroup][i % kMaxGroup] = kNegInf;
-      sm.split.bp[i / kMaxGroup][i % kMaxGroup] = 0.f;
-    }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
@@ -809,21 +797,20 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   const float *vpool = static_cast<const float *>(a.v_pool);
   const int Hkv = a.num_kv_heads;
 
-  float m_run[kMaxGroup], l_run[kMaxGroup], bmass[kMaxGroup], acc[kMaxGroup][CPL];
+  float m_run[kMaxGroup], l_run[kMaxGroup], cmass[kMaxGroup], acc[kMaxGroup][CPL];
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     m_run[h] = kNegInf;
     l_run[h] = 0.f;
-    bmass[h] = 0.f;
+    cmass[h] = 0.f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) acc[h][j] = 0.f;
   }
 
-  for (int i = 0; chunk_live(blocked, c_begin, c_end, w, i); ++i) {
-    const int pos = chunk_of(blocked, c_begin, w, i);
-    if (want_mass && i % kChunksPerBlock == 0)
+  for (int i = 0; chunk_live(c_begin, c_end, w, i); ++i) {
+    const int pos = chunk_of(c_begin, w, i);
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) bmass[h] = 0.f;
+    for (int h = 0; h < kMaxGroup; ++h) cmass[h] = 0.f;
     int page, sub, valid;
     if (pos < c_end && resolve_chunk(a, b, g, T, pos, page, sub, valid)) {
       const int64_t tile = (int64_t)page * Hkv + g;
@@ -860,12 +847,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) ps += __shfl_xor(ps, o);
         l_run[h] = l_run[h] * alpha[h] + ps;
-        bmass[h] = bmass[h] * alpha[h] + ps;
+        cmass[h] = ps;
         m_run[h] = m_new;
       }
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        const float *vrow = vpool + (tile * D + lane + 64 * j) * kBlockTokens + sub * kChunkTokens;
+        const float *vrow = vpool + ((tile * kChunksPerBlock + sub) * D + lane + 64 * j) * kChunkTokens;
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h)
           if (h < G) acc[h][j] *= alpha[h];
@@ -883,12 +870,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
       }
     }
     if (want_mass && lane == 0) {
-      const int nl = w + kWaves * (i / kChunksPerBlock);
+      const int cl = w + kWaves * i;
 #pragma unroll
       for (int h = 0; h < kMaxGroup; ++h)
         if (h < G) {
-          sm.split.bm[nl][h] = m_run[h];
-          sm.split.bp[nl][h] = bmass[h];
+          sm.split.cm[cl][h] = m_run[h];
+          sm.split.cp[cl][h] = cmass[h];
         }
     }
   }

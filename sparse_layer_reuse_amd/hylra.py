@@ -22,6 +22,7 @@ LIB_PATH = os.environ.get("HYLRA_LIBRARY") or os.path.join(_HERE, "libhylra.so")
 OK, E_INVALID_ARG, E_UNSUPPORTED, E_BAD_POLICY, E_WORKSPACE, E_DEVICE = range(6)
 F32, BF16 = 0, 1
 BLOCK = 128
+SUBTILE = 32  # tokens per V sub-tile
 
 
 class HylraError(RuntimeError):
@@ -131,14 +132,27 @@ def make_shape(q: torch.Tensor, k_pool: torch.Tensor, table: torch.Tensor, scale
     return Shape(B, Hq, k_pool.shape[1], d, BLOCK, _DTYPES[q.dtype], table.shape[1], float(scale))
 
 
+def check_pool_shapes(k_shape, v_shape):
+    """Raises ValueError unless K is [pages][Hkv][128][d] and V the matching
+    [pages][Hkv][4][d][32] (four 32-token sub-tiles per page, each
+    dimension-major)."""
+    k_shape, v_shape = tuple(k_shape), tuple(v_shape)
+    ok = len(k_shape) == 4 and k_shape[2] == BLOCK
+    if ok:
+        P, Hkv, _, d = k_shape
+        ok = v_shape == (P, Hkv, BLOCK // SUBTILE, d, SUBTILE)
+    if not ok:
+        raise ValueError("K pool must be [pages][Hkv][128][d] and V pool [pages][Hkv][4][d][32] "
+                         "(got %s and %s)" % (k_shape, v_shape))
+
+
 def make_kv(k_pool, v_pool, table, ctx) -> KV:
     _need(k_pool, "k_pool", tuple(_DTYPES), 4)
-    _need(v_pool, "v_pool", k_pool.dtype, 4)
+    _need(v_pool, "v_pool", k_pool.dtype, 5)
     _need(table, "block_table", torch.int32, 2)
     _need(ctx, "ctx_lens", torch.int32, 1)
-    P, Hkv, blk, d = k_pool.shape
-    if blk != BLOCK or tuple(v_pool.shape) != (P, Hkv, d, BLOCK):
-        raise ValueError("K pool must be [pages][Hkv][128][d] and V pool [pages][Hkv][d][128]")
+    check_pool_shapes(k_pool.shape, v_pool.shape)
+    P = k_pool.shape[0]
     if ctx.shape[0] != table.shape[0]:
         raise ValueError("ctx_lens and block_table disagree on the batch size")
     return KV(k_pool.data_ptr(), v_pool.data_ptr(), P, table.data_ptr(), ctx.data_ptr())

@@ -16,7 +16,7 @@ Recipe (per layer l of a workload with base seed S):
     workload's element type (round-to-nearest-even for bfloat16);
   * block table: identity (sequence b, block n -> page b*N+n) or, when paged,
     a PCG64 permutation (seed S+4) of all pages.
-Layouts: q [B][Hq][d], K [pages][Hkv][128][d], V [pages][Hkv][d][128].
+Layouts: q [B][Hq][d], K [pages][Hkv][128][d], V [pages][Hkv][4][d][32].
 """
 from __future__ import annotations
 
@@ -24,6 +24,8 @@ import numpy as np
 import torch
 
 from .workloads import BLOCK, Workload
+
+SUBTILE = 32  # tokens per V sub-tile
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -95,7 +97,8 @@ def make_layer(*, batch, num_q_heads, num_kv_heads, head_dim, dtype, ctx_lens,
     G = Hq // Hkv
     q = torch.randn(B, Hq, d, generator=_gen(device, seed + 0), device=device)
     k = torch.randn(num_pages, Hkv, BLOCK, d, generator=_gen(device, seed + 1), device=device)
-    v = torch.randn(num_pages, Hkv, d, BLOCK, generator=_gen(device, seed + 2), device=device)
+    v = torch.randn(num_pages, Hkv, BLOCK // SUBTILE, d, SUBTILE, generator=_gen(device, seed + 2),
+                    device=device)
     if hot is not None and alpha != 0.0:
         u = q.view(B, Hkv, G, d).sum(dim=2)
         u = u / u.norm(dim=-1, keepdim=True)

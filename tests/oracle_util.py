@@ -2,6 +2,7 @@
 import numpy as np
 
 BLOCK = 128
+SUB = 32  # tokens per V sub-tile: V pages are [Hkv][4][d][32]
 
 
 def dense_kv(layer_np, b, num_kv_heads):
@@ -17,7 +18,7 @@ def dense_kv(layer_np, b, num_kv_heads):
     for t in range(T):
         page = table[b, t // BLOCK]
         K[:, t, :] = kf[page, :, t % BLOCK, :]
-        V[:, t, :] = vf[page, :, :, t % BLOCK]
+        V[:, t, :] = vf[page, :, (t % BLOCK) // SUB, :, t % SUB]
     return K, V
 
 
@@ -33,9 +34,9 @@ def pools_from_dense(K, V, dtype=np.float32):
     Hkv, T, d = K.shape
     nb = max(1, (T + BLOCK - 1) // BLOCK)
     kp = np.zeros((nb, Hkv, BLOCK, d), dtype)
-    vp = np.zeros((nb, Hkv, d, BLOCK), dtype)
+    vp = np.zeros((nb, Hkv, BLOCK // SUB, d, SUB), dtype)
     for t in range(T):
         kp[t // BLOCK, :, t % BLOCK, :] = K[:, t, :]
-        vp[t // BLOCK, :, :, t % BLOCK] = V[:, t, :]
+        vp[t // BLOCK, :, (t % BLOCK) // SUB, :, t % SUB] = V[:, t, :]
     table = np.arange(nb, dtype=np.int32)[None, :]
     return kp, vp, table

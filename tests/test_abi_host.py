@@ -190,3 +190,18 @@ def test_policy_dp_golden():
         force = [j in case["force"] for j in range(L)]
         src, r, _ = H.policy_dp(M, float(np.float32(case["theta"])), force)
         assert src == case["src"] and r == case["resets"], case
+
+
+def test_binding_pool_layout_check():
+    """The binding accepts exactly the layouts the header documents, and the
+    seeded generator produces them."""
+    H.check_pool_shapes((10, 2, 128, 64), (10, 2, 4, 64, 32))
+    for k_shape, v_shape in [((10, 2, 128, 64), (10, 2, 64, 128)),      # whole-page V tile
+                             ((10, 2, 128, 64), (10, 2, 4, 32, 64)),     # token-major sub-tile
+                             ((10, 2, 64, 64), (10, 2, 2, 64, 32)),      # 64-token pages
+                             ((10, 2, 128, 64), (9, 2, 4, 64, 32))]:
+        with pytest.raises(ValueError):
+            H.check_pool_shapes(k_shape, v_shape)
+    lay = synth.make_layer(batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, dtype="f32",
+                           ctx_lens=[300], seed=3)
+    H.check_pool_shapes(lay["k_pool"].shape, lay["v_pool"].shape)

@@ -209,14 +209,32 @@ def test_decode_sparse_all_blocks_equals_full(H):
     assert (lse_s - lse_f).abs().max().item() <= 1e-5
 
 
-def check_policy_run(H, layers_gpu, src, k, dtype, num_kv_heads, check_layers=None):
-    """Run the GPU policy and compare the chosen layers with the oracle."""
+def sampled_sequences(layer, seqs):
+    """Oracle inputs for a subset of a layer's sequences: their q rows and
+    context lengths, and only the pages their block-table rows name, gathered
+    into a compact pool with the table renumbered to match."""
+    bs = torch.as_tensor(list(seqs), device=layer["q"].device)
+    table = layer["table"][bs]
+    pages = table.reshape(-1).long()
+    assert bool((pages >= 0).all()), "sampled tables must name pages only"
+    return {"q": layer["q"][bs], "k_pool": layer["k_pool"][pages],
+            "v_pool": layer["v_pool"][pages],
+            "table": torch.arange(pages.numel(), dtype=torch.int32,
+                                  device=pages.device).view(table.shape),
+            "ctx": layer["ctx"][bs]}
+
+
+def check_policy_run(H, layers_gpu, src, k, dtype, num_kv_heads, check_layers=None, seqs=None):
+    """Run the GPU policy and compare the chosen layers (and, with ``seqs``,
+    only those sequences) with the oracle."""
     bufs = [nan_out(l["q"]) for l in layers_gpu]
     outs, lses, idx_log = H.run_policy(layers_gpu, src, k, outs=[b[0] for b in bufs],
                                        lses=[b[1] for b in bufs])
     first = layers_gpu[0]
     assert counters_are_zero(H, first["q"], first["k_pool"], first["table"], k)
     idx_gpu = idx_log.cpu().numpy()
+    pick = (lambda a: a) if seqs is None else (lambda a: a[list(seqs)])
+    idx_gpu = pick(idx_gpu.transpose(1, 0, 2, 3)).transpose(1, 0, 2, 3)
     tol = TOL[dtype]
     L = len(layers_gpu)
     check = range(L) if check_layers is None else check_layers
@@ -225,7 +243,9 @@ def check_policy_run(H, layers_gpu, src, k, dtype, num_kv_heads, check_layers=No
         need = j in check or any(src[x] == j for x in check)
         if not need:
             continue
-        o = synth.layer_to_oracle(layers_gpu[j])
+        lay = layers_gpu[j] if seqs is None else sampled_sequences(layers_gpu[j], seqs)
+        o = synth.layer_to_oracle(lay)
+        del lay
         if src[j] == j:
             r_out, r_lse, score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
                                                      o["ctx"], num_kv_heads=num_kv_heads)
@@ -240,9 +260,10 @@ def check_policy_run(H, layers_gpu, src, k, dtype, num_kv_heads, check_layers=No
             assert np.array_equal(idx_gpu[j], idx_gpu[src[j]]), "layer %d: carried set" % j
             r_out, r_lse, _ = oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"],
                                             o["ctx"], num_kv_heads=num_kv_heads, sel=carried, k=k)
+        del o
         if j in check:
-            assert_close(outs[j].cpu().numpy(), r_out, tol, "layer %d out" % j)
-            assert_close(lses[j].cpu().numpy(), r_lse, tol, "layer %d lse" % j)
+            assert_close(pick(outs[j].cpu().numpy()), r_out, tol, "layer %d out" % j)
+            assert_close(pick(lses[j].cpu().numpy()), r_lse, tol, "layer %d lse" % j)
             checked += 1
     return checked, outs, lses, idx_log
 
@@ -340,3 +361,63 @@ def test_run_policy_graph_replays_match_eager(H):
         assert torch.equal(plan.idx_log, ref_idx), "replay %d idx" % rep
         eager.run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def workload_src(H, wl, theta=None):
+    """Per-layer source list of a workload: fixed resets, or the policy DP on
+    its similarity matrix (the library's DP must agree with the oracle's)."""
+    if wl.policy == "fixed":
+        return W.src_from_resets(wl.layers, wl.resets)
+    theta = wl.dp_theta[0] if theta is None else theta
+    M = synth.workload_similarity(wl)
+    force = [j in wl.dp_force for j in range(wl.layers)]
+    src, nres, _ = oracle.policy_dp(M, theta, force)
+    src_lib, nres_lib, _ = H.policy_dp(M, theta, force)
+    assert list(src_lib) == list(src) and nres_lib == nres
+    return list(src)
+
+
+PREFIX = 8
+
+
+@pytest.mark.parametrize("name,k,theta", [
+    ("llama3_8b_b8_64k_dp", 32, None),
+    ("llama3_8b_paged_128k", 8, None),
+    ("llama3_8b_paged_128k", 32, None),
+    ("llama3_8b_paged_128k", 64, None),
+    ("llama3_70b_128k_dp", 32, 0.8),
+    ("llama3_70b_128k_dp", 32, 0.7),
+    ("llama3_70b_128k_dp", 32, 0.9),
+])
+def test_run_policy_large_workload_prefix(H, name, k, theta):
+    """The large workloads at full per-layer size (batch, context, heads,
+    paging) in the benchmark's launch configuration: the first layers of the
+    step under the workload's policy (eight, or more until two reuse layers
+    are in), checked for the first and the last sequence of the batch."""
+    wl = W.get(name)
+    full_src = workload_src(H, wl, theta)
+    L = PREFIX  # at least eight layers, more until two of them reuse
+    while L < wl.layers and sum(1 for j in range(L) if full_src[j] != j) < 2:
+        L += 1
+    src = full_src[:L]
+    resets = sum(1 for j, s_ in enumerate(src) if s_ == j)
+    assert resets >= 2 and L - resets >= 2, src
+    say("run_policy", name, "k", k, "theta", theta, "layers 0-%d" % (L - 1), "src", src)
+    layers = synth.workload_layers(wl, device="cuda", layers=range(L))
+    seqs = sorted({0, wl.batch - 1})
+    n, outs, lses, idx_log = check_policy_run(H, layers, src, k, wl.dtype, wl.num_kv_heads,
+                                              seqs=seqs)
+    assert n == L
+    # the planted hot blocks dominate the selection of the reset layers
+    hot = synth.workload_hot_sets(wl)
+    for j in range(L):
+        if src[j] != j:
+            continue
+        for b in seqs:
+            want = set(hot[j][b].tolist())
+            for g in range(wl.num_kv_heads):
+                got = set(idx_log[j, b, g].tolist())
+                if k >= len(want):
+                    assert want <= got, "layer %d seq %d head %d" % (j, b, g)
+                else:
+                    assert got <= want, "layer %d seq %d head %d" % (j, b, g)
