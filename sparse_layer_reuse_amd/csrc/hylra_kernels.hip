@@ -201,6 +201,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return (int)x + base;
 }
 
+__device__ __forceinline__ bool wave_any(bool c) { return __ballot(c) != 0; }
+
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
@@ -223,36 +225,53 @@ struct EpiSmem {
   float invL[kMaxGroup];
   f32x4 red[kThreads];
   uint32_t keys[kMaxBlocks];
-  int hist[256];
+  int hist[2][kWaves][256];  // top-k digit histograms (two sets, per wavefront)
+  uint32_t kor[kWaves], kand[kWaves];
+  int seg_gt[kWaves], seg_eq[kWaves];
 };
 
 // Selects the k_eff = min(k, N) largest keys[0..N) (unsigned compare), equal
 // keys going to the lower index, and writes their indices in ascending order
-// to out[0..k_eff), -1 after.  Run by ONE wavefront (no workgroup barrier):
-// keys must already be in LDS and visible to it.  Radix select over 4 x 8
-// bits (digits shared by every key are skipped) with a histogram private to
-// the wavefront finds the k_eff-th largest key `thr`; keys above thr are
-// taken, keys equal to thr in index order until k_eff (compaction by rows of
-// 64 blocks with ballots).
-__device__ __forceinline__ void select_topk_wave(EpiSmem &sm, int N, int k, int32_t *out) {
-  const int lane = threadIdx.x & 63;
+// to out[0..k_eff), -1 after.  Called by every thread of the workgroup once
+// the keys are in LDS and a barrier has made them visible.
+//   threshold  radix select over 4 x 8 bits, most significant digit first;
+//              digits shared by every key are skipped.  Each wavefront counts
+//              the digits of its keys into a private 256-bin histogram (two
+//              sets, alternating between passes, so one barrier per pass
+//              suffices); every wavefront then sums the eight histograms and
+//              finds the same digit on its own.
+//   compaction each wavefront owns a contiguous segment of the keys and takes
+//              those above the threshold, and those equal to it in index
+//              order until k_eff; ballots give positions inside a row of 64,
+//              per-wavefront counts the offset of each segment.
+__device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int32_t *out) {
+  const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int keff = k < N ? k : N;
   if (keff == N) {  // every block is selected (also N == 0)
-    for (int r = lane; r < k; r += 64) out[r] = r < N ? r : -1;
+    for (int r = threadIdx.x; r < k; r += kThreads) out[r] = r < N ? r : -1;
     return;
   }
   uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-  for (int n = lane; n < N; n += 64) {
+  for (int n = threadIdx.x; n < N; n += kThreads) {
     kor |= sm.keys[n];
     kand &= sm.keys[n];
   }
   kor = wave_or(kor);
   kand = wave_and(kand);
+  if (lane == 0) {
+    sm.kor[w] = kor;
+    sm.kand[w] = kand;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    kor |= sm.kor[v];
+    kand &= sm.kand[v];
+  }
   const uint32_t common = ~(kor ^ kand);
-  int *hist = sm.hist;
 
   uint32_t prefix = 0u, mask = 0u;
-  int remaining = keff;
+  int remaining = keff, npass = 0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t dmask = 255u << shift;
@@ -261,19 +280,27 @@ __device__ __forceinline__ void select_topk_wave(EpiSmem &sm, int N, int k, int3
       mask |= dmask;
       continue;
     }
-    *reinterpret_cast<u32x4 *>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+    int(*hist)[256] = sm.hist[npass & 1];
+    ++npass;
+    *reinterpret_cast<u32x4 *>(&hist[w][4 * lane]) = u32x4{0u, 0u, 0u, 0u};
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    for (int n = lane; n < N; n += 64) {
+    for (int n = threadIdx.x; n < N; n += kThreads) {
       const uint32_t kv = sm.keys[n];
-      if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1);
+      if ((kv & mask) == prefix) atomicAdd(&hist[w][(kv >> shift) & 255u], 1);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // lane l holds bins 255-4l .. 252-4l (descending); find the bin where the
-    // count of keys from the top reaches `remaining`
-    const u32x4 hv = *reinterpret_cast<const u32x4 *>(&hist[252 - 4 * lane]);
-    const int c[4] = {(int)hv[3], (int)hv[2], (int)hv[1], (int)hv[0]};
+    __syncthreads();
+    // lane l sums bins 255-4l .. 252-4l (descending) over the wavefronts and
+    // finds the bin where the count of keys from the top reaches `remaining`
+    int c[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const u32x4 hv = *reinterpret_cast<const u32x4 *>(&hist[v][252 - 4 * lane]);
+      c[0] += (int)hv[3];
+      c[1] += (int)hv[2];
+      c[2] += (int)hv[1];
+      c[3] += (int)hv[0];
+    }
     const int tot = c[0] + c[1] + c[2] + c[3];
     int above = wave_inclusive_scan(tot) - tot;
     int digit = -1, rem = 0;
@@ -289,18 +316,39 @@ __device__ __forceinline__ void select_topk_wave(EpiSmem &sm, int N, int k, int3
     prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, leader) << shift;
     mask |= dmask;
     remaining = __builtin_amdgcn_readlane(rem, leader);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();  // bins are reused by the next pass
   }
   const uint32_t thr = prefix;
   const int need_eq = remaining;
 
-  int taken = 0, eq_before = 0;
-  for (int base = 0; base < N; base += 64) {
+  // segment of wavefront w: rows of 64 keys [w*seg, min(N, (w+1)*seg))
+  const int seg = ((N + kWaves - 1) / kWaves + 63) / 64 * 64;
+  const int n0 = w * seg, n1 = min(N, n0 + seg);
+  int gt = 0, eq = 0;
+  for (int base = n0; base < n1; base += 64) {
     const int n = base + lane;
-    const uint32_t kv = n < N ? sm.keys[n] : 0u;
-    const bool is_gt = n < N && kv > thr;
-    const bool is_eq = n < N && kv == thr;
+    const uint32_t kv = n < n1 ? sm.keys[n] : 0u;
+    gt += __builtin_popcountll(__ballot(n < n1 && kv > thr));
+    eq += __builtin_popcountll(__ballot(n < n1 && kv == thr));
+  }
+  if (lane == 0) {
+    sm.seg_gt[w] = gt;
+    sm.seg_eq[w] = eq;
+  }
+  __syncthreads();
+  int taken = 0, eq_before = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    if (v < w) {
+      const int e = sm.seg_eq[v];
+      taken += sm.seg_gt[v] + min(e, max(0, need_eq - eq_before));
+      eq_before += e;
+    }
+  }
+  for (int base = n0; base < n1; base += 64) {
+    const int n = base + lane;
+    const uint32_t kv = n < n1 ? sm.keys[n] : 0u;
+    const bool is_gt = n < n1 && kv > thr;
+    const bool is_eq = n < n1 && kv == thr;
     const uint64_t eqm = __ballot(is_eq);
     const bool sel = is_gt || (is_eq && eq_before + lanes_below(eqm) < need_eq);
     const uint64_t selm = __ballot(sel);
@@ -308,7 +356,7 @@ __device__ __forceinline__ void select_topk_wave(EpiSmem &sm, int N, int k, int3
     taken += __builtin_popcountll(selm);
     eq_before += __builtin_popcountll(eqm);
   }
-  for (int r = keff + lane; r < k; r += 64) out[r] = -1;
+  for (int r = keff + threadIdx.x; r < k; r += kThreads) out[r] = -1;
 }
 
 template <int D>
@@ -318,7 +366,7 @@ union KernelSmem {
 };
 
 // Outputs of a (b, g) with no chunk to attend (empty context).
-__device__ void write_empty(const AttnArgs &a, int b, int g, int D) {
+__device__ __forceinline__ void write_empty(const AttnArgs &a, int b, int g, int D) {
   const int G = a.group;
   for (int i = threadIdx.x; i < G * D; i += kThreads)
     a.out[((int64_t)b * a.num_q_heads + g * G) * D + i] = 0.f;
@@ -343,7 +391,7 @@ __device__ void write_empty(const AttnArgs &a, int b, int g, int D) {
 // counts the workgroup's arrival.  Returns true in the last of the nact
 // workgroups of (b, g), which then runs the epilogue.
 template <int D>
-__device__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact, int c_begin,
+__device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact, int c_begin,
                              int c_end, int T, SplitSmem<D> &sm, int *last_flag) {
   const int G = a.group;
   const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
@@ -412,13 +460,19 @@ __device__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact, i
 // workgroup of (b, g) to finish its split pass.
 //
 // out: thread -> (head h, 4 columns c) item and a stripe of the splits.  The
-// first batch of partial outputs and the first block masses are loaded before
-// the (max, sum) pass, so the loads travel together.
-template <int D>
-__device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
-  constexpr int kBatch = 8;
+// loads that do not depend on each other are issued up front, in the order
+// they are needed: the (max, sum) partials, the first batch of partial
+// outputs, the block masses of block threadIdx.x.  They are straight-line
+// code (a branch around a load makes the compiler wait for the load at the
+// join), sized by the template arguments so that few are wasted: kBatch
+// split partials per thread, masses of GP >= G heads.  Loads needed only by
+// larger shapes (a second head per wavefront, more than 64 splits, blocks
+// past kThreads) sit behind branches.  A lane out of range reads at an
+// offset past the resource, which gives 0 without touching memory.
+template <int D, int kBatch, int GP>
+__device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
   const int G = a.group;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
   const int items = G * (D / 4);  // <= kThreads
   const int stripes = kThreads / items;
@@ -427,8 +481,7 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
   const int h_item = item / (D / 4), c_item = 4 * (item % (D / 4));
   const __amdgpu_buffer_rsrc_t po = buffer(a.part_o + head0 * a.nsplit * D,
                                            (uint32_t)(G * a.nsplit * D * 4));
-  // loads of splits stripe + stripes * (j0 + j); out of range: an offset past
-  // the resource, which reads 0 without touching memory
+  // loads of splits stripe + stripes * (j0 + j)
   auto load_batch = [&](f32x4 (&v)[kBatch], int j0) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -439,36 +492,78 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
       v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(po, off, 0, kCoherent));
     }
   };
+  const int N = (T + kBlockTokens - 1) / kBlockTokens;
+  // (max, sum) of the splits of heads w and w + kWaves (one wavefront a head)
+  const __amdgpu_buffer_rsrc_t pml = buffer(a.part_ml + head0 * a.nsplit * 2,
+                                            (uint32_t)(G * a.nsplit * 2 * 4));
+  auto load_ml = [&](int hh, int j, float &m, float &l) {
+    const int h = w + kWaves * hh, s = lane + 64 * j;
+    const bool in = h < G && s < nact;
+    // two 32-bit loads: this toolchain compiles the 64-bit raw buffer load
+    // builtin into a single 32-bit load whose word fills both halves
+    const uint32_t off = in ? (uint32_t)((h * a.nsplit + s) * 2 * 4) : 0x80000000u;
+    const uint32_t m_bits = __builtin_amdgcn_raw_buffer_load_b32(pml, off, 0, kCoherent);
+    const uint32_t l_bits = __builtin_amdgcn_raw_buffer_load_b32(pml, off + 4u, 0, kCoherent);
+    m = in ? __builtin_bit_cast(float, m_bits) : kNegInf;
+    l = in ? __builtin_bit_cast(float, l_bits) : 0.f;
+  };
+  constexpr int HH = GP > kWaves ? 2 : 1;  // heads per wavefront
+  float ms[HH][kMaxSplits / 64], ls[HH][kMaxSplits / 64];
+  load_ml(0, 0, ms[0][0], ls[0][0]);
   f32x4 first[kBatch];
   load_batch(first, 0);
-  const int N = (T + kBlockTokens - 1) / kBlockTokens;
-  float mass0[kMaxGroup];
+  // block masses (stored relative to their split's max) of block threadIdx.x
+  const __amdgpu_buffer_rsrc_t pst =
+      buffer(a.stats != nullptr ? a.stats + head0 * a.max_blocks : nullptr,
+             a.stats != nullptr ? (uint32_t)(G * a.max_blocks * 4) : 0u);
+  float mass_pre[GP];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-    mass0[h] = (a.stats != nullptr && h < G && (int)threadIdx.x < N)
-                   ? load_agent(a.stats + (head0 + h) * a.max_blocks + threadIdx.x)
-                   : 0.f;
-
-  // per head: global max / sum and the per-split rescale factors
-  for (int h = w; h < G; h += kWaves) {
-    const float *ml = a.part_ml + (head0 + h) * a.nsplit * 2;
-    float ms[kMaxSplits / 64], ls[kMaxSplits / 64];
-    float mx = kNegInf;
+  for (int h = 0; h < GP; ++h) {
+    const int n = threadIdx.x;
+    const uint32_t off = (h < G && n < N) ? (uint32_t)((h * a.max_blocks + n) * 4) : 0x80000000u;
+    mass_pre[h] =
+        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pst, off, 0, kCoherent));
+  }
+  // masses of block threadIdx.x + kThreads (more than kThreads blocks)
+  float mass_pre1[GP];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) mass_pre1[h] = 0.f;
+  if (a.stats != nullptr && N > kThreads) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const int n = threadIdx.x + kThreads;
+      const uint32_t off =
+          (h < G && n < N) ? (uint32_t)((h * a.max_blocks + n) * 4) : 0x80000000u;
+      mass_pre1[h] =
+          __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pst, off, 0, kCoherent));
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < HH; ++hh)
 #pragma unroll
     for (int j = 0; j < kMaxSplits / 64; ++j) {
-      const int s = lane + 64 * j;
-      ms[j] = s < nact ? load_agent(ml + 2 * s) : kNegInf;
-      ls[j] = s < nact ? load_agent(ml + 2 * s + 1) : 0.f;
-      mx = fmaxf(mx, ms[j]);
+      if (hh == 0 && j == 0) continue;
+      ms[hh][j] = kNegInf;
+      ls[hh][j] = 0.f;
+      if (w + kWaves * hh < G && 64 * j < nact) load_ml(hh, j, ms[hh][j], ls[hh][j]);
     }
+
+  // per head: global max / sum and the per-split rescale factors
+#pragma unroll
+  for (int hh = 0; hh < HH; ++hh) {
+    const int h = w + kWaves * hh;
+    if (h >= G) continue;
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kMaxSplits / 64; ++j) mx = fmaxf(mx, ms[hh][j]);
     const float M = wave_max(mx);
     float lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxSplits / 64; ++j) {
       const int s = lane + 64 * j;
-      const float f = rescale(ms[j], M);
+      const float f = rescale(ms[hh][j], M);
       if (s < nact) sm.f[h][s] = f;
-      lsum += f * ls[j];
+      lsum += f * ls[hh][j];
     }
     const float L = wave_sum(lsum);
     if (lane == 0) {
@@ -536,10 +631,11 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
     if (n < N) {
       const int s = n / blocks_per_split;
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
+      for (int h = 0; h < GP; ++h) {
         if (h >= G) continue;
-        const float mass = n < kThreads ? mass0[h]
-                                        : load_agent(a.stats + (head0 + h) * a.max_blocks + n);
+        const float mass = n < kThreads       ? mass_pre[h]
+                           : n < 2 * kThreads ? mass_pre1[h]
+                                              : load_agent(a.stats + (head0 + h) * a.max_blocks + n);
         score += mass * sm.f[h][s] * sm.invL[h];
       }
       sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
@@ -551,11 +647,39 @@ __device__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSm
     }
   }
   __syncthreads();
-  if (a.idx_out != nullptr && w == 0)
-    select_topk_wave(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
+  if (a.idx_out != nullptr)
+    select_topk_block(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
   if (a.score_out != nullptr && (int)threadIdx.x < a.max_blocks)
     a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + threadIdx.x] = score0;
   store_outputs();
+}
+
+// Picks the epilogue instance whose load counts fit (b, g): kBatch >= the
+// split partials per thread (2, 4 or 8; more run in further batches), GP >= G.
+// Only the bf16 kernel with d = 128 (the large shapes) gets the specialised
+// instances; the others use one generic instance.
+template <int D, bool kSpecialise>
+__device__ __forceinline__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
+  if constexpr (!kSpecialise) {
+    epilogue_impl<D, 8, kMaxGroup>(a, b, g, T, nact, sm);
+  } else {
+    const int G = a.group;
+    const int stripes = kThreads / (G * (D / 4));
+    const int per = (nact + stripes - 1) / stripes;
+    const int nb = per <= 2 ? 0 : per <= 4 ? 1 : 2;
+    const int gp = G <= 4 ? 0 : G <= 8 ? 1 : 2;
+    switch (uniform(3 * nb + gp)) {
+      case 0: epilogue_impl<D, 2, 4>(a, b, g, T, nact, sm); break;
+      case 1: epilogue_impl<D, 2, 8>(a, b, g, T, nact, sm); break;
+      case 2: epilogue_impl<D, 2, 16>(a, b, g, T, nact, sm); break;
+      case 3: epilogue_impl<D, 4, 4>(a, b, g, T, nact, sm); break;
+      case 4: epilogue_impl<D, 4, 8>(a, b, g, T, nact, sm); break;
+      case 5: epilogue_impl<D, 4, 16>(a, b, g, T, nact, sm); break;
+      case 6: epilogue_impl<D, 8, 4>(a, b, g, T, nact, sm); break;
+      case 7: epilogue_impl<D, 8, 8>(a, b, g, T, nact, sm); break;
+      default: epilogue_impl<D, 8, 16>(a, b, g, T, nact, sm); break;
+    }
+  }
 }
 
 // Common prologue: range of the workgroup, early exits.  Returns false if the
@@ -766,7 +890,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int r = 0; r < 4; ++r) sm.split.o[w][4 * quad + r][16 * n + m16] = acc[n][r];
   __syncthreads();
   if (!finish_split<D>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
-  epilogue<D>(a, b, g, T, r.nact, sm.epi);
+  epilogue<D, D == 128>(a, b, g, T, r.nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -892,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   }
   __syncthreads();
   if (!finish_split<D>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
-  epilogue<D>(a, b, g, T, r.nact, sm.epi);
+  epilogue<D, false>(a, b, g, T, r.nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -910,7 +1034,7 @@ __global__ __launch_bounds__(kThreads) void score_topk(TopkArgs a) {
     sm.keys[n] = sc > 0.f ? __float_as_uint(sc) : 0u;
   }
   __syncthreads();
-  if (threadIdx.x < 64) select_topk_wave(sm, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k);
+  select_topk_block(sm, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k);
 }
 
 // Kernel timers: while a timer runs, each launch of its kind takes an event
