@@ -97,7 +97,8 @@ int max_nsplit(const hylra_shape *s, int k) {
   int n = f.nsplit;
   if (k > 0) {
     const hylra::SplitPlan p =
-        hylra::plan_sparse(s->batch, s->num_kv_heads, s->max_blocks_per_seq, k);
+        hylra::plan_sparse(s->batch, s->num_kv_heads, s->max_blocks_per_seq, k,
+                           s->num_q_heads / s->num_kv_heads, s->head_dim);
     if (p.nsplit > n) n = p.nsplit;
   }
   return n;
@@ -187,7 +188,8 @@ hylra_status run_sparse(const hylra_shape *s, const void *q, const hylra_kv *kv,
                         const int32_t *idx, int k, float *out, float *lse, int32_t *log,
                         const Workspace &w, void *stream) {
   const hylra::SplitPlan plan =
-      hylra::plan_sparse(s->batch, s->num_kv_heads, s->max_blocks_per_seq, k);
+      hylra::plan_sparse(s->batch, s->num_kv_heads, s->max_blocks_per_seq, k,
+                         s->num_q_heads / s->num_kv_heads, s->head_dim);
   hylra::AttnArgs a = attn_args(s, q, kv, idx, k, plan, w);
   a.out = out;
   a.lse = lse;
@@ -201,19 +203,23 @@ hylra_status run_sparse(const hylra_shape *s, const void *q, const hylra_kv *kv,
 namespace hylra {
 
 // Split plans: about 256 workgroups per launch (one 8-wavefront workgroup
-// resident per compute unit on a 256-CU part), each taking a multiple of 8
-// chunks (one per wavefront; in full mode also whole 128-token blocks, so a
-// block's mass never straddles two workgroups).  At most kMaxSplits workgroups
-// per (sequence, KV head) and kMaxWgChunks chunks per workgroup.
+// resident per compute unit on a 256-CU part) and at most kMaxWgChunks chunks
+// per workgroup.  Full mode: a multiple of 8 chunks per workgroup (one per
+// wavefront, and whole 128-token blocks, so a block's mass never straddles
+// two workgroups), at most kMaxSplits workgroups per (sequence, KV head).
+// Sparse mode: a multiple of 4 chunks, so a small selection spreads over
+// more compute units with one busy wavefront per SIMD (two wavefronts on one
+// SIMD share its vector issue), but at most as many splits as the merge reads
+// with one batch of 8 partial loads per thread (8 * 512 / (G * d / 4)).
 static_assert(kWavesPerGroup % kChunksPerBlock == 0, "a workgroup unit must hold whole blocks");
 constexpr long kTargetWorkgroups = 256;
 
-static SplitPlan make_plan(long chunks_per_seq, long rows, long unit) {
+static SplitPlan make_plan(long chunks_per_seq, long rows, long unit, long max_splits) {
   long cpw = (rows * chunks_per_seq + kTargetWorkgroups - 1) / kTargetWorkgroups;
-  const long min_cpw = (chunks_per_seq + kMaxSplits - 1) / kMaxSplits;
+  const long min_cpw = (chunks_per_seq + max_splits - 1) / max_splits;
   if (cpw < min_cpw) cpw = min_cpw;
   cpw = (cpw + unit - 1) / unit * unit;
-  if (cpw > kMaxWgChunks) cpw = kMaxWgChunks;  // min_cpw <= 128 always
+  if (cpw > kMaxWgChunks) cpw = kMaxWgChunks;  // nsplit <= 4 * 8192 / 256 <= kMaxSplits
   SplitPlan p;
   p.chunks_per_wg = (int)cpw;
   p.nsplit = (int)((chunks_per_seq + cpw - 1) / cpw);
@@ -222,13 +228,17 @@ static SplitPlan make_plan(long chunks_per_seq, long rows, long unit) {
 
 SplitPlan plan_full(int batch, int num_kv_heads, int max_blocks) {
   return make_plan((long)kChunksPerBlock * max_blocks, (long)batch * num_kv_heads,
-                   (long)kWavesPerGroup);
+                   (long)kWavesPerGroup, (long)kMaxSplits);
 }
 
-SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k) {
+SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k, int group,
+                      int head_dim) {
   const long keff = k < max_blocks ? k : max_blocks;
+  const long items = (long)group * head_dim / 4;  // merge threads per split
+  long max_splits = 8 * (items < 512 ? 512 / items : 1);
+  if (max_splits > kMaxSplits) max_splits = kMaxSplits;
   return make_plan((long)kChunksPerBlock * (keff > 0 ? keff : 1), (long)batch * num_kv_heads,
-                   (long)kWavesPerGroup);
+                   (long)kChunksPerBlock, max_splits);
 }
 
 }  // namespace hylra

@@ -25,7 +25,7 @@ struct SplitPlan {
 };
 
 SplitPlan plan_full(int batch, int num_kv_heads, int max_blocks);
-SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k);
+SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k, int group, int head_dim);
 
 // Arguments of the attention kernels (split pass + fused epilogue).
 struct AttnArgs {
