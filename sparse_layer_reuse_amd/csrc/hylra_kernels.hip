@@ -46,6 +46,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 (raw 32-bit data) on gfx9
 constexpr int kCoherent = 16;             // buffer instruction cache policy: sc1
+constexpr int kStreaming = 2;             // buffer instruction cache policy: nt (read once)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -783,10 +784,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int k = 0; k < D / 32; ++k)
-        t.k[h][k] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane, (4 * h * D + 32 * k) * 2, 0);
+        t.k[h][k] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane, (4 * h * D + 32 * k) * 2,
+                                                          kStreaming);
 #pragma unroll
     for (int n = 0; n < D / 16; ++n)
-      t.v[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_lane, n * 16 * kChunkTokens * 2, 0);
+      t.v[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_lane, n * 16 * kChunkTokens * 2,
+                                                     kStreaming);
     return valid;
   };
 
