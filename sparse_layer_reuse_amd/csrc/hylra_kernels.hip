@@ -226,25 +226,45 @@ struct EpiSmem {
   float invL[kMaxGroup];
   f32x4 red[kThreads];
   uint32_t keys[kMaxBlocks];
-  int hist[2][kWaves][256];  // top-k digit histograms (two sets, per wavefront)
+  int hist[4][kWaves][256];  // top-k digit histograms (one set per radix pass, per wavefront)
   uint32_t kor[kWaves], kand[kWaves];
   int seg_gt[kWaves], seg_eq[kWaves];
 };
 
+// Top-k preparation, done by every thread while it writes its keys:
+// clears the digit histograms of all passes and gathers the AND / OR of the
+// keys (topk_note per key, topk_publish once per thread before the barrier
+// that makes the keys visible).
+__device__ __forceinline__ void topk_clear(EpiSmem &sm) {
+  int *h = &sm.hist[0][0][0];
+  for (int i = 4 * threadIdx.x; i < 4 * kWaves * 256; i += 4 * kThreads)
+    *reinterpret_cast<u32x4 *>(&h[i]) = u32x4{0u, 0u, 0u, 0u};
+}
+__device__ __forceinline__ void topk_publish(EpiSmem &sm, uint32_t kor, uint32_t kand) {
+  kor = wave_or(kor);
+  kand = wave_and(kand);
+  if ((threadIdx.x & 63) == 0) {
+    sm.kor[threadIdx.x >> 6] = kor;
+    sm.kand[threadIdx.x >> 6] = kand;
+  }
+}
+
 // Selects the k_eff = min(k, N) largest keys[0..N) (unsigned compare), equal
 // keys going to the lower index, and writes their indices in ascending order
-// to out[0..k_eff), -1 after.  Called by every thread of the workgroup once
-// the keys are in LDS and a barrier has made them visible.
+// to out[0..k_eff), -1 after.  Called by every thread of the workgroup after
+// topk_clear / topk_publish and a barrier that made the keys visible.
 //   threshold  radix select over 4 x 8 bits, most significant digit first;
-//              digits shared by every key are skipped.  Each wavefront counts
-//              the digits of its keys into a private 256-bin histogram (two
-//              sets, alternating between passes, so one barrier per pass
-//              suffices); every wavefront then sums the eight histograms and
-//              finds the same digit on its own.
+//              digits shared by every key are skipped, and the passes stop
+//              once the chosen digit's bucket is taken whole.  Each wavefront
+//              counts the digits of its keys into a private 256-bin
+//              histogram of the pass (cleared beforehand, so one barrier per
+//              pass suffices); every wavefront then sums the eight histograms
+//              and finds the same digit on its own.
 //   compaction each wavefront owns a contiguous segment of the keys and takes
-//              those above the threshold, and those equal to it in index
-//              order until k_eff; ballots give positions inside a row of 64,
-//              per-wavefront counts the offset of each segment.
+//              those whose decided bits are above the threshold, and those
+//              equal to it in index order until k_eff; ballots give positions
+//              inside a row of 64, per-wavefront counts the offset of each
+//              segment.
 __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int32_t *out) {
   const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int keff = k < N ? k : N;
@@ -253,17 +273,6 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
     return;
   }
   uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-  for (int n = threadIdx.x; n < N; n += kThreads) {
-    kor |= sm.keys[n];
-    kand &= sm.keys[n];
-  }
-  kor = wave_or(kor);
-  kand = wave_and(kand);
-  if (lane == 0) {
-    sm.kor[w] = kor;
-    sm.kand[w] = kand;
-  }
-  __syncthreads();
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) {
     kor |= sm.kor[v];
@@ -272,7 +281,7 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
   const uint32_t common = ~(kor ^ kand);
 
   uint32_t prefix = 0u, mask = 0u;
-  int remaining = keff, npass = 0;
+  int remaining = keff;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t dmask = 255u << shift;
@@ -281,11 +290,7 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
       mask |= dmask;
       continue;
     }
-    int(*hist)[256] = sm.hist[npass & 1];
-    ++npass;
-    *reinterpret_cast<u32x4 *>(&hist[w][4 * lane]) = u32x4{0u, 0u, 0u, 0u};
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    int(*hist)[256] = sm.hist[pass];
     for (int n = threadIdx.x; n < N; n += kThreads) {
       const uint32_t kv = sm.keys[n];
       if ((kv & mask) == prefix) atomicAdd(&hist[w][(kv >> shift) & 255u], 1);
@@ -304,12 +309,13 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
     }
     const int tot = c[0] + c[1] + c[2] + c[3];
     int above = wave_inclusive_scan(tot) - tot;
-    int digit = -1, rem = 0;
+    int digit = -1, rem = 0, cnt = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (above < remaining && remaining <= above + c[i]) {
         digit = 255 - 4 * lane - i;
         rem = remaining - above;
+        cnt = c[i];
       }
       above += c[i];
     }
@@ -317,6 +323,7 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
     prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, leader) << shift;
     mask |= dmask;
     remaining = __builtin_amdgcn_readlane(rem, leader);
+    if (remaining == __builtin_amdgcn_readlane(cnt, leader)) break;  // bucket taken whole
   }
   const uint32_t thr = prefix;
   const int need_eq = remaining;
@@ -327,7 +334,7 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
   int gt = 0, eq = 0;
   for (int base = n0; base < n1; base += 64) {
     const int n = base + lane;
-    const uint32_t kv = n < n1 ? sm.keys[n] : 0u;
+    const uint32_t kv = n < n1 ? sm.keys[n] & mask : 0u;
     gt += __builtin_popcountll(__ballot(n < n1 && kv > thr));
     eq += __builtin_popcountll(__ballot(n < n1 && kv == thr));
   }
@@ -347,7 +354,7 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
   }
   for (int base = n0; base < n1; base += 64) {
     const int n = base + lane;
-    const uint32_t kv = n < n1 ? sm.keys[n] : 0u;
+    const uint32_t kv = n < n1 ? sm.keys[n] & mask : 0u;
     const bool is_gt = n < n1 && kv > thr;
     const bool is_eq = n < n1 && kv == thr;
     const uint64_t eqm = __ballot(is_eq);
@@ -549,6 +556,9 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
       if (w + kWaves * hh < G && 64 * j < nact) load_ml(hh, j, ms[hh][j], ls[hh][j]);
     }
 
+  // the top-k histograms are cleared while the loads are in flight
+  if (a.idx_out != nullptr) topk_clear(sm);
+
   // per head: global max / sum and the per-split rescale factors
 #pragma unroll
   for (int hh = 0; hh < HH; ++hh) {
@@ -627,6 +637,7 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
   // (mass stored relative to its split's max; f brings it to the head's max)
   const int blocks_per_split = a.chunks_per_wg / kChunksPerBlock;
   float score0 = 0.f;  // score of block n = thread, stored after the barrier
+  uint32_t kor = 0u, kand = 0xFFFFFFFFu;
   for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
     float score = 0.f;
     if (n < N) {
@@ -639,7 +650,10 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
                                               : load_agent(a.stats + (head0 + h) * a.max_blocks + n);
         score += mass * sm.f[h][s] * sm.invL[h];
       }
-      sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
+      const uint32_t key = score > 0.f ? __float_as_uint(score) : 0u;
+      sm.keys[n] = key;
+      kor |= key;
+      kand &= key;
     }
     if (n < kThreads) {
       score0 = score;
@@ -647,6 +661,7 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
       a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = score;
     }
   }
+  if (a.idx_out != nullptr) topk_publish(sm, kor, kand);
   __syncthreads();
   if (a.idx_out != nullptr)
     select_topk_block(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
@@ -1032,10 +1047,16 @@ __global__ __launch_bounds__(kThreads) void score_topk(TopkArgs a) {
   const int N = (T + kBlockTokens - 1) / kBlockTokens;
   __shared__ EpiSmem sm;
   const float *row = a.score + ((int64_t)b * a.num_kv_heads + g) * a.max_blocks;
+  topk_clear(sm);
+  uint32_t kor = 0u, kand = 0xFFFFFFFFu;
   for (int n = threadIdx.x; n < N; n += kThreads) {
     const float sc = row[n];
-    sm.keys[n] = sc > 0.f ? __float_as_uint(sc) : 0u;
+    const uint32_t key = sc > 0.f ? __float_as_uint(sc) : 0u;
+    sm.keys[n] = key;
+    kor |= key;
+    kand &= key;
   }
+  topk_publish(sm, kor, kand);
   __syncthreads();
   select_topk_block(sm, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k);
 }
