@@ -421,3 +421,77 @@ def test_run_policy_large_workload_prefix(H, name, k, theta):
                     assert want <= got, "layer %d seq %d head %d" % (j, b, g)
                 else:
                     assert got <= want, "layer %d seq %d head %d" % (j, b, g)
+
+
+# The bf16 d=128 merge is compiled in instances sized by the split partials
+# each merge thread reads (ceil(splits / stripes), stripes = 512 / (G * d / 4)
+# threads per split: up to 2, 4, 8, 16 and more) and by the group size bound
+# (4, 8, 16).  With one KV head and a context of 256 * n tokens a sequence
+# gets n splits of eight 32-token chunks, so these cases reach every
+# instance, in full mode with the fused top-k and in sparse mode.
+INSTANCE_CASES = [
+    # (group, splits)
+    (4, 6), (4, 12), (4, 24), (4, 40),
+    (8, 3), (8, 6), (8, 12), (8, 20),
+    (16, 2), (16, 3), (16, 6), (16, 10),
+    (2, 12), (5, 7), (12, 9),
+]
+
+
+@pytest.mark.parametrize("G,nsplit", INSTANCE_CASES, ids=lambda v: str(v))
+def test_merge_instances_full_with_topk(H, G, nsplit):
+    ctx = (256 * nsplit - 100,)
+    say("merge instance full G", G, "splits", nsplit, "ctx", ctx)
+    lay = gpu_layer("bf16", ctx, G, 1, 128, seed=900 + 7 * G + nsplit,
+                    hot=[[0, (ctx[0] - 1) // 128]], alpha=2.0)
+    k = 3
+    outs, lses, idx_log = H.run_policy([lay], [0], k, outs=[nan_out(lay["q"])[0]],
+                                       lses=[nan_out(lay["q"])[1]])
+    assert counters_are_zero(H, lay["q"], lay["k_pool"], lay["table"], k)
+    o = synth.layer_to_oracle(lay)
+    r_out, r_lse, r_score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
+                                               o["ctx"], num_kv_heads=1)
+    assert_close(outs[0].cpu().numpy(), r_out, TOL["bf16"], "out")
+    assert_close(lses[0].cpu().numpy(), r_lse, TOL["bf16"], "lse")
+    want, margin = oracle.topk(r_score, o["ctx"], k)
+    got = idx_log[0].cpu().numpy()
+    near = margin < MARGIN
+    assert np.all(np.all(got == want, axis=-1) | near), (got, want)
+
+
+@pytest.mark.parametrize("G,k", [(4, 2), (4, 16), (4, 40), (8, 2), (8, 8), (8, 30),
+                                 (16, 2), (16, 4), (16, 16), (16, 40)], ids=lambda v: str(v))
+def test_merge_instances_sparse(H, G, k):
+    ctx = (128 * 64 - 50,)
+    say("merge instance sparse G", G, "k", k)
+    lay = gpu_layer("bf16", ctx, G, 1, 128, seed=700 + 5 * G + k)
+    rng = np.random.default_rng(G * 100 + k)
+    sel = np.sort(rng.choice(64, size=min(k, 64), replace=False)).astype(np.int32)
+    sel = np.concatenate([sel, np.full(k - len(sel), -1, np.int32)])[None, None, :]
+    o0, l0 = nan_out(lay["q"])
+    out, lse = H.decode_sparse(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
+                               torch.from_numpy(sel).cuda(), out=o0, lse=l0)
+    assert counters_are_zero(H, lay["q"], lay["k_pool"], lay["table"], k)
+    o = synth.layer_to_oracle(lay)
+    r_out, r_lse, _ = oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
+                                    num_kv_heads=1, sel=sel, k=k)
+    assert_close(out.cpu().numpy(), r_out, TOL["bf16"], "out")
+    assert_close(lse.cpu().numpy(), r_lse, TOL["bf16"], "lse")
+
+
+def test_merge_generic_instance_d64_many_splits(H):
+    """bf16 with d = 64 uses the generic merge instance; 40 splits with 8
+    heads per KV head need several batches of partial loads."""
+    ctx = (256 * 40 - 3, 5000)
+    say("merge generic d64", ctx)
+    lay = gpu_layer("bf16", ctx, 16, 2, 64, seed=77)
+    k = 5
+    outs, lses, idx_log = H.run_policy([lay], [0], k)
+    o = synth.layer_to_oracle(lay)
+    r_out, r_lse, r_score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
+                                               o["ctx"], num_kv_heads=2)
+    assert_close(outs[0].cpu().numpy(), r_out, TOL["bf16"], "out")
+    assert_close(lses[0].cpu().numpy(), r_lse, TOL["bf16"], "lse")
+    want, margin = oracle.topk(r_score, o["ctx"], k)
+    got = idx_log[0].cpu().numpy()
+    assert np.all(np.all(got == want, axis=-1) | (margin < MARGIN))
