@@ -146,6 +146,45 @@ def graph_timed(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps, graph
 
 
+def step_percentiles(graph, steps, torch):
+    """Per-step times of `steps` graph replays, each bracketed by its own
+    events: (p10, p50, p90) in ms."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    pick = lambda q: t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))]
+    return pick(0.1), pick(0.5), pick(0.9)
+
+
+def stream_ceiling(torch, hylra, mib=512, buffers=4, reps=3):
+    """Practical HBM read ceiling: the library's read probe (the attention
+    kernels' K/V load pattern, no arithmetic) over `buffers` distinct
+    `mib`-MiB buffers in turn, so no launch finds its data in a cache."""
+    bufs = [torch.ones(mib << 20, dtype=torch.uint8, device="cuda") for _ in range(buffers)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        hylra.read_probe(b, sink)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        for b in bufs:
+            hylra.read_probe(b, sink)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop)
+    launches = reps * buffers
+    del bufs
+    return {"gbs": launches * (mib << 20) / (ms * 1e-3) / 1e9, "bytes_per_launch": mib << 20,
+            "launches": launches, "kernel": "read_probe (hylra_read_probe)"}
+
+
 def cpu_baseline(wl, layers, src, k, budget_s):
     """Oracle timed on the host: passes over the step's layers in order (the
     carried indices flow from each reset layer to its reuse layers) until the
@@ -226,8 +265,11 @@ def main():
     # eager steps with per-kernel HIP events (per-layer latency, roofline)
     ms_eager, kern = timed(hybrid.run, args.steps, args.warmup, torch, ALL, hylra)
     # the step as one HIP graph (how a decode loop replays a static step): value
-    ms_h, _ = graph_timed(hybrid.run, args.steps, args.warmup, torch)
-    result_extra = {"eager_steps_per_s": 1000.0 / ms_eager, "eager_ms_per_step": ms_eager}
+    ms_h, graph_h = graph_timed(hybrid.run, args.steps, args.warmup, torch)
+    p10, p50, p90 = step_percentiles(graph_h, args.steps, torch)
+    del graph_h
+    result_extra = {"eager_steps_per_s": 1000.0 / ms_eager, "eager_ms_per_step": ms_eager,
+                    "step_ms_p10_p50_p90": [p10, p50, p90]}
     if not args.skip_baselines:
         full = hylra.FullPlan(layers)
         _, kern_f = timed(full.run, args.steps, args.warmup, torch,
@@ -295,6 +337,10 @@ def main():
         "input_generation_s": gen_s,
     }
     out.update(result_extra)
+    if not args.skip_baselines:
+        ceil = stream_ceiling(torch, hylra)
+        out["stream_ceiling"] = ceil
+        out["roofline"]["frac_of_stream_ceiling"] = achieved / ceil["gbs"]
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(wl, layers, src, k, args.cpu_seconds)
     else:

@@ -160,6 +160,16 @@ hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
 hylra_status hylra_timer_start(int32_t kind, int32_t capacity);
 hylra_status hylra_timer_stop(int32_t kind, double *total_ms, int32_t *launches);
 
+/* Diagnostic: reads `bytes` (a positive multiple of 16) of device memory at
+ * `buf` (16-byte aligned) once, with the loads and cache policy of the
+ * attention kernels' K/V stream (16-byte non-temporal buffer loads, 512-thread
+ * workgroups each reading a contiguous 2 MiB range), and folds the data into
+ * a value stored to the device word `sink` only when it equals a constant the
+ * callers never produce.  Timing it gives the practical HBM read ceiling
+ * against which the attention kernels' bandwidth is set.  Asynchronous on
+ * `hip_stream`. */
+hylra_status hylra_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *hip_stream);
+
 /* Static string for a status code. */
 const char *hylra_status_str(hylra_status status);
 

@@ -407,6 +407,15 @@ hylra_status hylra_timer_start(int32_t kind, int32_t capacity) {
   return ok();
 }
 
+hylra_status hylra_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *hip_stream) {
+  if (buf == nullptr || sink == nullptr) return fail(HYLRA_E_INVALID_ARG, "read probe: null pointer");
+  if (!aligned16(buf)) return fail(HYLRA_E_INVALID_ARG, "read probe: buffer must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+    return fail(HYLRA_E_INVALID_ARG, "read probe: bytes must be a positive multiple of 16 (got %zu)",
+                bytes);
+  return device_status(hylra::launch_read_probe(buf, bytes, sink, hip_stream), "read probe launch");
+}
+
 hylra_status hylra_timer_stop(int32_t kind, double *total_ms, int32_t *launches) {
   if (kind < 0 || kind >= hylra::kNumTimers) return fail(HYLRA_E_INVALID_ARG, "unknown timer kind %d", kind);
   int n = 0;

@@ -71,6 +71,7 @@ struct TopkArgs {
 // Launchers: return 0 on success or the hipError_t code of the launch.
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream);
 int launch_topk(const TopkArgs &a, int batch, void *stream);
+int launch_read_probe(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
 const char *device_error_string(int code);
 
 // Kernel timers (see hylra_timer_start in hylra.h).

@@ -1143,6 +1143,37 @@ int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *str
   return (int)hipGetLastError();
 }
 
+// Read probe: each workgroup streams a contiguous range with the K/V loads
+// of the attention kernels (16-byte non-temporal buffer loads, four in
+// flight per lane) and folds them into one word that is stored only if the
+// fold hits a value the probe's callers never place in memory.
+constexpr uint32_t kProbeBytesPerWg = 2u << 20;
+__global__ __launch_bounds__(kThreads) void read_probe(const char *base, uint64_t bytes,
+                                                       uint32_t *sink) {
+  const uint64_t begin = (uint64_t)blockIdx.x * kProbeBytesPerWg;
+  const uint64_t left = bytes - begin;
+  const uint32_t span = left < kProbeBytesPerWg ? (uint32_t)left : kProbeBytesPerWg;
+  const __amdgpu_buffer_rsrc_t r = buffer(base + begin, span);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  constexpr uint32_t kStep = kThreads * 16 * 4;
+  for (uint32_t off = threadIdx.x * 16; off < span; off += kStep) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off + u * kThreads * 16, 0, kStreaming);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u];
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = blockIdx.x;
+}
+
+int launch_read_probe(const void *buf, uint64_t bytes, uint32_t *sink, void *stream) {
+  const unsigned grid = (unsigned)((bytes + kProbeBytesPerWg - 1) / kProbeBytesPerWg);
+  hipLaunchKernelGGL(read_probe, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const char *>(buf), bytes, sink);
+  return (int)hipGetLastError();
+}
+
 int launch_topk(const TopkArgs &a, int batch, void *stream) {
   const TimerScope tm(kTimerTopk);
   hipExtLaunchKernelGGL(score_topk, dim3(a.num_kv_heads, batch), dim3(kThreads), 0,

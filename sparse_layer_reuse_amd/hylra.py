@@ -60,6 +60,7 @@ def _load():
         "hylra_policy_dp": [I32, P, ctypes.c_float, P, P, P, P],
         "hylra_timer_start": [I32, I32],
         "hylra_timer_stop": [I32, P, P],
+        "hylra_read_probe": [P, SZ, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -76,7 +77,7 @@ _lib = _load()
 
 EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
             "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_timer_start",
-            "hylra_timer_stop", "hylra_status_str", "hylra_last_error")
+            "hylra_timer_stop", "hylra_read_probe", "hylra_status_str", "hylra_last_error")
 
 KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_TOPK = range(3)
 KERNEL_NAMES = {KERNEL_FULL_ATTN: "attn_full_layer", KERNEL_SPARSE_ATTN: "attn_sparse_layer",
@@ -299,6 +300,16 @@ def policy_dp(M, theta: float, force=None):
                                 src.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nres),
                                 ctypes.byref(sim)))
     return src.tolist(), int(nres.value), float(sim.value)
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Stream every byte of `buf` (a 16-byte aligned GPU tensor) once with the
+    attention kernels' K/V load pattern (practical read-ceiling probe); `sink`
+    is a one-word int32 GPU tensor."""
+    _need(buf, "buf")
+    _need(sink, "sink", torch.int32)
+    _check(_lib.hylra_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                 sink.data_ptr(), _stream(stream)))
 
 
 def timer_start(kind: int, capacity: int = 4096) -> None:

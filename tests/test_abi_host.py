@@ -205,3 +205,13 @@ def test_binding_pool_layout_check():
     lay = synth.make_layer(batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, dtype="f32",
                            ctx_lens=[300], seed=3)
     H.check_pool_shapes(lay["k_pool"].shape, lay["v_pool"].shape)
+
+
+def test_read_probe_argument_checks():
+    lib = H._lib
+    sink = ctypes.c_uint32(0)
+    assert lib.hylra_read_probe(None, 1024, ctypes.addressof(sink), None) == H.E_INVALID_ARG
+    assert lib.hylra_read_probe(0x10000, 1024, None, None) == H.E_INVALID_ARG
+    assert lib.hylra_read_probe(0x10008, 1024, ctypes.addressof(sink), None) == H.E_INVALID_ARG
+    assert lib.hylra_read_probe(0x10000, 0, ctypes.addressof(sink), None) == H.E_INVALID_ARG
+    assert lib.hylra_read_probe(0x10000, 1000, ctypes.addressof(sink), None) == H.E_INVALID_ARG
