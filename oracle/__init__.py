@@ -201,6 +201,41 @@ def run_policy(layers, src, k, *, num_kv_heads, scale=None):
 
 
 # ---------------------------------------------------------------------------
+# Offline profiling: the similarity matrix from logged index sets (summary 2.2)
+# ---------------------------------------------------------------------------
+def overlap_matrix(idx_log):
+    """Similarity of the top-k index sets between layers, measured offline.
+
+    Summary 2.2 builds a lower-triangular matrix M from the overlap ratio of
+    the top-k indices of layer pairs on profiling data.  ``idx_log`` is
+    ``[P][L][S][k]`` int (P profiling steps, L layers, S = sequences x KV
+    heads, each row the layer's selected block ids, -1 padded).  Read here:
+    one slice is (step, sequence, KV head); its ratio for source layer i and
+    target layer j >= i is |I_i n I_j| / |I_j|, and M[j][i] is the mean of
+    that ratio over the slices whose target set is not empty, summed in
+    float64 in slice order (p, then s); 0 when every target set is empty,
+    and 0 above the diagonal.  Returns a float32 [L][L] array.
+    """
+    idx = np.asarray(idx_log)
+    P, L, S, _ = idx.shape
+    sets = [[[set(int(x) for x in idx[p, l, s] if x >= 0) for s in range(S)]
+             for l in range(L)] for p in range(P)]
+    M = np.zeros((L, L), dtype=np.float32)
+    for j in range(L):
+        for i in range(j + 1):
+            total, used = 0.0, 0
+            for p in range(P):
+                for s in range(S):
+                    tgt = sets[p][j][s]
+                    if not tgt:
+                        continue
+                    total += len(sets[p][i][s] & tgt) / len(tgt)
+                    used += 1
+            M[j, i] = np.float32(total / used) if used else np.float32(0.0)
+    return M
+
+
+# ---------------------------------------------------------------------------
 # Offline policy optimisation (summary 2.2)
 # ---------------------------------------------------------------------------
 SIM_TIE = 1e-12
