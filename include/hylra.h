@@ -160,6 +160,21 @@ hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
 hylra_status hylra_timer_start(int32_t kind, int32_t capacity);
 hylra_status hylra_timer_stop(int32_t kind, double *total_ms, int32_t *launches);
 
+/* Offline similarity matrix for the policy program (section 2.2: M is built
+ * from the overlap ratio of the layers' top-k indices on profiling data).
+ * idx_log: device [steps][num_layers][slices][k] int32, each row a layer's
+ * selected block ids in ascending order, -1 padded (for example the idx_log
+ * of hylra_run_policy with every layer resetting, slices = B * Hkv, one
+ * entry per profiling step).  M: device [num_layers][num_layers] float32,
+ * row = target layer j, column = source layer i: for i <= j the mean over
+ * the slices (step, sequence, KV head) whose target set is not empty of
+ * |I_i n I_j| / |I_j|, summed in float64 in slice order; 0 if every target
+ * set is empty, and 0 above the diagonal.  1 <= num_layers <= 1024,
+ * num_layers * k <= 16000 (HYLRA_E_UNSUPPORTED beyond).  Asynchronous on
+ * `hip_stream`; hylra_policy_dp takes M once copied to the host. */
+hylra_status hylra_overlap_matrix(int32_t steps, int32_t num_layers, int32_t slices, int32_t k,
+                                  const int32_t *idx_log, float *M, void *hip_stream);
+
 /* Diagnostic: reads `bytes` (a positive multiple of 16) of device memory at
  * `buf` (16-byte aligned) once, with the loads and cache policy of the
  * attention kernels' K/V stream (16-byte non-temporal buffer loads, 512-thread

@@ -407,6 +407,22 @@ hylra_status hylra_timer_start(int32_t kind, int32_t capacity) {
   return ok();
 }
 
+hylra_status hylra_overlap_matrix(int32_t steps, int32_t num_layers, int32_t slices, int32_t k,
+                                  const int32_t *idx_log, float *M, void *hip_stream) {
+  if (idx_log == nullptr || M == nullptr) return fail(HYLRA_E_INVALID_ARG, "overlap: null pointer");
+  if (steps < 1 || slices < 1 || k < 1 || num_layers < 1 || num_layers > 1024)
+    return fail(HYLRA_E_INVALID_ARG,
+                "overlap: need steps >= 1, 1 <= layers <= 1024, slices >= 1, k >= 1 "
+                "(got %d, %d, %d, %d)", steps, num_layers, slices, k);
+  if (hylra::overlap_smem_bytes(num_layers, k) > 65536)
+    return fail(HYLRA_E_UNSUPPORTED, "overlap: layers * k = %lld exceeds 16000",
+                (long long)num_layers * k);
+  if ((reinterpret_cast<uintptr_t>(idx_log) & 3u) || (reinterpret_cast<uintptr_t>(M) & 3u))
+    return fail(HYLRA_E_INVALID_ARG, "overlap: pointers must be 4-byte aligned");
+  hylra::OverlapArgs a{idx_log, steps, num_layers, slices, k, M};
+  return device_status(hylra::launch_overlap(a, hip_stream), "overlap launch");
+}
+
 hylra_status hylra_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *hip_stream) {
   if (buf == nullptr || sink == nullptr) return fail(HYLRA_E_INVALID_ARG, "read probe: null pointer");
   if (!aligned16(buf)) return fail(HYLRA_E_INVALID_ARG, "read probe: buffer must be 16-byte aligned");

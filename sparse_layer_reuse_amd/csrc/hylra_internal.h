@@ -72,6 +72,15 @@ struct TopkArgs {
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream);
 int launch_topk(const TopkArgs &a, int batch, void *stream);
 int launch_read_probe(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
+
+// Offline similarity matrix of logged top-k index sets (hylra_profile.hip).
+struct OverlapArgs {
+  const int32_t *idx;  // [steps][layers][slices][k], ascending ids, -1 padded
+  int steps, layers, slices, k;
+  float *M;  // [layers][layers], row = target layer
+};
+size_t overlap_smem_bytes(int layers, int k);
+int launch_overlap(const OverlapArgs &a, void *stream);
 const char *device_error_string(int code);
 
 // Kernel timers (see hylra_timer_start in hylra.h).

@@ -61,6 +61,7 @@ def _load():
         "hylra_timer_start": [I32, I32],
         "hylra_timer_stop": [I32, P, P],
         "hylra_read_probe": [P, SZ, P, P],
+        "hylra_overlap_matrix": [I32, I32, I32, I32, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -77,7 +78,8 @@ _lib = _load()
 
 EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
             "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_timer_start",
-            "hylra_timer_stop", "hylra_read_probe", "hylra_status_str", "hylra_last_error")
+            "hylra_timer_stop", "hylra_overlap_matrix", "hylra_read_probe", "hylra_status_str",
+            "hylra_last_error")
 
 KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_TOPK = range(3)
 KERNEL_NAMES = {KERNEL_FULL_ATTN: "attn_full_layer", KERNEL_SPARSE_ATTN: "attn_sparse_layer",
@@ -300,6 +302,25 @@ def policy_dp(M, theta: float, force=None):
                                 src.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nres),
                                 ctypes.byref(sim)))
     return src.tolist(), int(nres.value), float(sim.value)
+
+
+def overlap_matrix(idx_log: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Offline similarity matrix M [L][L] (row = target layer) of logged index
+    sets idx_log [P][L][S][k] int32 (P profiling steps, S slices)."""
+    _need(idx_log, "idx_log", torch.int32, 4)
+    t = idx_log.contiguous()
+    P, L, S, k = t.shape
+    if out is None:
+        out = torch.empty(L, L, dtype=torch.float32, device=t.device)
+    _check(_lib.hylra_overlap_matrix(P, L, S, k, t.data_ptr(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def profiling_log(policy_logs) -> torch.Tensor:
+    """Stacks the idx_log tensors [L][B][Hkv][k] of several profiling steps
+    of hylra_run_policy into the [P][L][B*Hkv][k] layout of overlap_matrix."""
+    logs = [l.reshape(l.shape[0], -1, l.shape[-1]) for l in policy_logs]
+    return torch.stack(logs).contiguous()
 
 
 def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

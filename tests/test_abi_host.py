@@ -215,3 +215,17 @@ def test_read_probe_argument_checks():
     assert lib.hylra_read_probe(0x10008, 1024, ctypes.addressof(sink), None) == H.E_INVALID_ARG
     assert lib.hylra_read_probe(0x10000, 0, ctypes.addressof(sink), None) == H.E_INVALID_ARG
     assert lib.hylra_read_probe(0x10000, 1000, ctypes.addressof(sink), None) == H.E_INVALID_ARG
+
+
+def test_overlap_matrix_argument_checks():
+    lib = H._lib
+    ok_ptr = 0x10000
+    assert lib.hylra_overlap_matrix(1, 4, 2, 8, None, ok_ptr, None) == H.E_INVALID_ARG
+    assert lib.hylra_overlap_matrix(1, 4, 2, 8, ok_ptr, None, None) == H.E_INVALID_ARG
+    assert lib.hylra_overlap_matrix(0, 4, 2, 8, ok_ptr, ok_ptr, None) == H.E_INVALID_ARG
+    assert lib.hylra_overlap_matrix(1, 0, 2, 8, ok_ptr, ok_ptr, None) == H.E_INVALID_ARG
+    assert lib.hylra_overlap_matrix(1, 1025, 2, 8, ok_ptr, ok_ptr, None) == H.E_INVALID_ARG
+    assert lib.hylra_overlap_matrix(1, 4, 0, 8, ok_ptr, ok_ptr, None) == H.E_INVALID_ARG
+    assert lib.hylra_overlap_matrix(1, 4, 2, 0, ok_ptr, ok_ptr, None) == H.E_INVALID_ARG
+    assert lib.hylra_overlap_matrix(1, 4, 2, 8, ok_ptr + 2, ok_ptr, None) == H.E_INVALID_ARG
+    assert lib.hylra_overlap_matrix(1, 1024, 2, 64, ok_ptr, ok_ptr, None) == H.E_UNSUPPORTED

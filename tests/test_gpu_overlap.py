@@ -1,0 +1,86 @@
+"""GPU parity of the offline similarity matrix (HyLRA technical summary 2.2)
+through the C ABI: bit-exact against the oracle (integer overlap counts,
+float64 ratio sums in slice order on both sides)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_layer_reuse_amd import synth, workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "overlap_worked.json")
+
+
+@pytest.fixture(scope="module")
+def H():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_layer_reuse_amd import hylra
+    return hylra
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def random_log(P, L, S, k, N, seed, empty_frac=0.0):
+    """Random ascending id sets with random valid counts (-1 padding)."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((P, L, S, k), -1, np.int32)
+    for p in range(P):
+        for s in range(S):
+            n = int(rng.integers(1, min(k, N) + 1))
+            if rng.random() < empty_frac:
+                n = 0
+            for l in range(L):
+                idx[p, l, s, :n] = np.sort(rng.choice(N, size=n, replace=False))
+    return idx
+
+
+def check(H, idx):
+    got = H.overlap_matrix(torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    want = oracle.overlap_matrix(idx)
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+def test_overlap_golden(H):
+    g = json.load(open(GOLDEN))
+    check(H, np.array(g["idx_log"], dtype=np.int32))
+
+
+@pytest.mark.parametrize("P,L,S,k,N", [(1, 1, 1, 1, 1), (1, 5, 3, 7, 20), (2, 12, 4, 16, 64),
+                                       (1, 32, 8, 32, 512), (3, 9, 5, 100, 300),
+                                       (1, 80, 8, 64, 1024), (2, 40, 2, 130, 4096)],
+                         ids=lambda v: str(v))
+def test_overlap_random(H, P, L, S, k, N):
+    say("overlap", P, L, S, k, N)
+    check(H, random_log(P, L, S, k, N, seed=P * 1000 + L * 10 + k, empty_frac=0.2))
+
+
+def test_overlap_from_all_reset_run(H):
+    """The offline loop on the drifting workload's first layers: an all-reset
+    step logs every layer's top-k, the matrix of those logs matches the
+    oracle's, and with k equal to the hot-set size the consecutive-layer
+    overlaps follow the planted drift."""
+    wl = W.LLAMA3_8B_B8_64K_DP
+    L = 6
+    say("overlap from all-reset run", wl.name, "layers", L)
+    layers = synth.workload_layers(wl, device="cuda", layers=range(L))
+    k = wl.hot_blocks
+    _, _, idx_log = H.run_policy(layers, list(range(L)), k)
+    log = H.profiling_log([idx_log])
+    got = H.overlap_matrix(log)
+    torch.cuda.synchronize()
+    want = oracle.overlap_matrix(log.cpu().numpy())
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+    hot = synth.workload_hot_sets(wl)
+    for j in range(1, L):
+        planted = np.mean([len(set(hot[j][b].tolist()) & set(hot[j - 1][b].tolist())) / k
+                           for b in range(wl.batch)])
+        assert abs(float(got[j, j - 1]) - planted) < 1e-6, (j, float(got[j, j - 1]), planted)
