@@ -9,6 +9,10 @@ beside it.  Also timed: the plain full-attention step (every layer full
 attention, no scores) and the all-reset step (every layer full attention +
 scores + top-k).
 
+Options beyond the timed default: --jump N (a static reset-every-N policy),
+--ctx T (context sweep), --profiled (policy from the DP on a similarity
+matrix measured on the GPU from an all-reset step's logged top-k sets).
+
 Prints one JSON line.  `value` is hybrid decode steps/s.  `roofline` covers
 the dominant kernel (full split attention of the reset layers): algorithmic
 bytes per launch = 4*B*Hkv*T*d (bf16 K and V, each read once), divided by its
@@ -43,6 +47,13 @@ def parse():
     p.add_argument("--topk", type=int, default=None)
     p.add_argument("--theta", type=float, default=None)
     p.add_argument("--layers", type=int, default=None, help="use only the first N layers")
+    p.add_argument("--ctx", type=int, default=None,
+                   help="override the context length of every sequence (context sweeps)")
+    p.add_argument("--jump", type=int, default=None, metavar="N",
+                   help="static policy: reset every N layers (a Jump-N baseline)")
+    p.add_argument("--profiled", action="store_true",
+                   help="policy from the DP on a similarity matrix profiled on the GPU "
+                        "(all-reset step, logged top-k overlaps) instead of the synthetic one")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget of the CPU oracle baseline (0 disables it)")
     p.add_argument("--skip-baselines", action="store_true",
@@ -84,8 +95,17 @@ def measured_traffic(workload):
     return rec.get("full_layer_traffic_bytes")
 
 
-def policy_for(wl, hylra, theta, L):
+def policy_for(wl, hylra, theta, L, jump=None, profiled_layers=None, k=None):
     from sparse_layer_reuse_amd import synth, workloads as W
+    if jump:
+        resets = tuple(range(0, wl.layers, jump))
+        return W.src_from_resets(wl.layers, resets)[:L], "jump %d" % jump, None
+    if profiled_layers is not None:
+        if theta is None:
+            theta = wl.dp_theta[0] if wl.dp_theta else 0.8
+        force = [j in wl.dp_force for j in range(L)] if wl.policy == "dp" else None
+        src, nres, _, _ = hylra.profile_policy([profiled_layers], k, theta, force)
+        return src, "dp on a profiled overlap matrix, theta=%g" % theta, theta
     if wl.policy == "fixed":
         src = W.src_from_resets(wl.layers, wl.resets)
         desc = "fixed resets %s" % (list(wl.resets),)
@@ -251,13 +271,18 @@ def main():
     from sparse_layer_reuse_amd import hylra, synth, workloads as W
 
     wl = W.get(args.workload)
+    if args.ctx:
+        import dataclasses
+        wl = dataclasses.replace(wl, name="%s_ctx%d" % (wl.name, args.ctx), ctx=args.ctx,
+                                 hot_blocks=min(wl.hot_blocks, (args.ctx + 127) // 128))
     k = args.topk or wl.topk[0]
     L = min(wl.layers, args.layers or wl.layers)
     t0 = time.time()
     layers = synth.workload_layers(wl, device="cuda", layers=range(L))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
-    src, policy_desc, theta = policy_for(wl, hylra, args.theta, L)
+    src, policy_desc, theta = policy_for(wl, hylra, args.theta, L, jump=args.jump,
+                                         profiled_layers=layers if args.profiled else None, k=k)
     n_reset = sum(1 for j, s in enumerate(src) if s == j)
 
     hybrid = hylra.PolicyPlan(layers, src, k)

@@ -333,6 +333,22 @@ def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
                                  sink.data_ptr(), _stream(stream)))
 
 
+def profile_policy(step_layers, k, theta, force=None):
+    """The offline loop of the technical summary 2.2 on profiling data: every
+    layer resets and logs its top-k (one hylra_run_policy per profiling step
+    in `step_layers`, a list of per-step layer lists), hylra_overlap_matrix
+    turns the logs into M, and hylra_policy_dp solves the policy.
+    Returns (src, num_resets, sim_sum, M as a host array)."""
+    logs = []
+    for layers in step_layers:
+        L = len(layers)
+        _, _, log = run_policy(layers, list(range(L)), k)
+        logs.append(log)
+    M = overlap_matrix(profiling_log(logs)).cpu().numpy()
+    src, nres, sim = policy_dp(M, theta, force)
+    return src, nres, sim, M
+
+
 def timer_start(kind: int, capacity: int = 4096) -> None:
     """Start bracketing every launch of a kernel kind with HIP events."""
     _check(_lib.hylra_timer_start(int(kind), int(capacity)))
