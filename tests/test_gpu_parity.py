@@ -495,3 +495,32 @@ def test_merge_generic_instance_d64_many_splits(H):
     want, margin = oracle.topk(r_score, o["ctx"], k)
     got = idx_log[0].cpu().numpy()
     assert np.all(np.all(got == want, axis=-1) | (margin < MARGIN))
+
+
+def test_max_context_fused_topk_and_reuse(H):
+    """The largest context the ABI takes: 8192 blocks (1M tokens) for one
+    sequence and KV head with 16 query heads; the reset layer's fused scores
+    and top-k (64 of 8192 blocks) and a reuse layer over them, against the
+    oracle."""
+    mb = 8192
+    ctx = (mb * 128,)
+    say("max context", ctx)
+    hot = [[5, 1000, 4097, 8191]]
+    layers = [gpu_layer("bf16", ctx, 16, 1, 128, seed=4242 + 16 * l, hot=hot, alpha=3.0)
+              for l in range(2)]
+    n, *_ = check_policy_run(H, layers, [0, 0], 64, "bf16", 1)
+    assert n == 2
+
+
+def test_max_rows_tiny_contexts(H):
+    """The largest number of (sequence, KV head) rows, 4096 x 16 = 65536,
+    with ragged contexts of 0..128 tokens, through a reset and a reuse
+    layer."""
+    B, Hkv = 4096, 16
+    rng = np.random.default_rng(11)
+    ctx = tuple(int(t) for t in rng.integers(0, 129, size=B))
+    say("max rows", B, "x", Hkv)
+    layers = [gpu_layer("bf16", ctx, Hkv, Hkv, 64, seed=5151 + 16 * l, max_blocks=1)
+              for l in range(2)]
+    n, *_ = check_policy_run(H, layers, [0, 0], 1, "bf16", Hkv)
+    assert n == 2
