@@ -425,7 +425,7 @@ def test_run_policy_large_workload_prefix(H, name, k, theta):
 
 # The bf16 d=128 merge is compiled in instances sized by the split partials
 # each merge thread reads (ceil(splits / stripes), stripes = 512 / (G * d / 4)
-# threads per split: up to 2, 4, 8, 16 and more) and by the group size bound
+# threads per split: up to 2, 4, 8 and more, in batches) and by the group size bound
 # (4, 8, 16).  With one KV head and a context of 256 * n tokens a sequence
 # gets n splits of eight 32-token chunks, so these cases reach every
 # instance, in full mode with the fused top-k and in sparse mode.
