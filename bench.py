@@ -360,6 +360,10 @@ def main():
             "avg_launch_us": full_us,
         },
         "input_generation_s": gen_s,
+        # the only speed figure the pages give: end-to-end (projections, MLP and
+        # attention), model and hardware not stated -- context, not this metric
+        "pages_context": {"speedup_vs_full_attention": 1.45, "scope": "end-to-end LLM decode",
+                          "sequence_length": 60000, "hardware": "not stated"},
     }
     out.update(result_extra)
     if not args.skip_baselines:
