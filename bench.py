@@ -51,6 +51,10 @@ def parse():
                    help="override the context length of every sequence (context sweeps)")
     p.add_argument("--jump", type=int, default=None, metavar="N",
                    help="static policy: reset every N layers (a Jump-N baseline)")
+    p.add_argument("--e2e", action="store_true",
+                   help="time a whole random-weight Llama-3-8B-shaped decode step (projections, "
+                        "RoPE, KV append, attention, MLP) for the hybrid and the full policy "
+                        "instead of attention alone")
     p.add_argument("--profiled", action="store_true",
                    help="policy from the DP on a similarity matrix profiled on the GPU "
                         "(all-reset step, logged top-k overlaps) instead of the synthetic one")
@@ -258,6 +262,37 @@ def cpu_baseline(wl, layers, src, k, budget_s):
     }
 
 
+def e2e(args, wl, k, src, policy_desc):
+    """End-to-end decode step of a random-weight decoder of the workload's
+    batch, context, heads and layer count, hybrid vs full attention."""
+    import torch
+    from sparse_layer_reuse_amd import decode_step as DS
+    import dataclasses
+    base = DS.shape_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim)
+    if base is None:
+        sys.exit("--e2e needs a Llama-3-8B or -70B head shape (workload %s)" % wl.name)
+    shape = dataclasses.replace(base, layers=len(src))
+    dec = DS.RandomDecoder(shape, wl.batch, wl.ctx, seed=wl.seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 99)
+    x = torch.randn(wl.batch, shape.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    ms_h, _ = graph_timed(lambda: dec.step(x, "hybrid", src, k), args.steps, args.warmup, torch)
+    ms_f, _ = graph_timed(lambda: dec.step(x, "full", src, k), args.steps, args.warmup, torch)
+    return {
+        "metric": "end-to-end decode steps/s, random-weight Llama-3-shaped model, hybrid vs full",
+        "value": 1000.0 / ms_h, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_h, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random weights, seeded KV history)",
+        "config": {"workload": wl.name, "batch": wl.batch, "ctx": wl.ctx, "layers": len(src),
+                   "hidden": shape.hidden, "ffn": shape.ffn, "topk": k, "policy": policy_desc},
+        "full_steps_per_s": 1000.0 / ms_f, "full_ms_per_step": ms_f,
+        "hybrid_over_full": ms_f / ms_h,
+        "pages_context": {"speedup_vs_full_attention": 1.45, "scope": "end-to-end LLM decode",
+                          "sequence_length": 60000, "hardware": "not stated"},
+    }
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -278,11 +313,18 @@ def main():
     k = args.topk or wl.topk[0]
     L = min(wl.layers, args.layers or wl.layers)
     t0 = time.time()
-    layers = synth.workload_layers(wl, device="cuda", layers=range(L))
+    layers = None
+    if args.profiled or not args.e2e:
+        layers = synth.workload_layers(wl, device="cuda", layers=range(L))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     src, policy_desc, theta = policy_for(wl, hylra, args.theta, L, jump=args.jump,
                                          profiled_layers=layers if args.profiled else None, k=k)
+    if args.e2e:
+        del layers
+        torch.cuda.empty_cache()
+        print(json.dumps(e2e(args, wl, k, src, policy_desc)), flush=True)
+        return
     n_reset = sum(1 for j, s in enumerate(src) if s == j)
 
     hybrid = hylra.PolicyPlan(layers, src, k)

@@ -1,0 +1,165 @@
+"""A decoder-only model step with random weights around the hybrid attention.
+
+This is the integration harness that puts the attention-only measurements in
+context (the pages report their speedup end to end, technical summary
+section 4): every layer of a Llama-3-shaped decoder runs RMSNorm, the QKV
+projection, rotary position embedding, the append of the new token's K and V
+into the paged cache, attention, the output projection and a SwiGLU MLP.  The
+projections and the MLP are plain library GEMMs (torch on hipBLASLt; each
+weight is stored in the layout whose batch-1..8 GEMV kernel streams fastest,
+and the residual adds ride in the GEMM's beta term) and a few torch
+elementwise ops (fused RMSNorm; RoPE with the step's cos/sin computed once);
+attention is this library: a reset
+layer runs hylra_run_policy on that one layer (full attention, fused block
+scores and top-k into the carried index buffer), a reuse layer runs
+hylra_decode_sparse over the carried indices, and the full-attention baseline
+runs hylra_decode_full on every layer.  Weights are random (no trained
+model); the step's shapes are static, so it can be captured as a HIP graph.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import hylra, synth
+
+BLOCK = 128
+SUBTILE = 32
+
+
+@dataclass(frozen=True)
+class DecoderShape:
+    layers: int
+    hidden: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    ffn: int
+    rope_theta: float = 500000.0
+
+
+LLAMA3_8B = DecoderShape(layers=32, hidden=4096, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         ffn=14336)
+LLAMA3_70B = DecoderShape(layers=80, hidden=8192, num_q_heads=64, num_kv_heads=8, head_dim=128,
+                          ffn=28672)
+
+
+def shape_for(num_q_heads: int, num_kv_heads: int, head_dim: int):
+    """The Llama-3 shape with these attention heads, or None."""
+    for s in (LLAMA3_8B, LLAMA3_70B):
+        if (s.num_q_heads, s.num_kv_heads, s.head_dim) == (num_q_heads, num_kv_heads, head_dim):
+            return s
+    return None
+
+
+EPS = 1e-5
+
+
+def rope_tables(pos: torch.Tensor, d: int, theta: float):
+    """cos / signed sin tables [B][1][d] of the rotate-half rotary embedding at
+    positions pos [B]: dimension i < d/2 pairs with i + d/2, both turned by
+    pos * theta^(-2i/d), so x' = x * C + roll(x, d/2) * S."""
+    inv = 1.0 / (theta ** (torch.arange(0, d, 2, device=pos.device, dtype=torch.float64) / d))
+    ang = pos.double()[:, None, None] * inv[None, None, :]
+    cos, sin = torch.cos(ang), torch.sin(ang)
+    return (torch.cat([cos, cos], -1).float().contiguous(),
+            torch.cat([-sin, sin], -1).float().contiguous())
+
+
+class RandomDecoder:
+    """Random-weight decoder with a paged KV cache holding `ctx` tokens per
+    sequence (the last one is written by each step)."""
+
+    def __init__(self, shape: DecoderShape, batch: int, ctx: int, *, seed: int = 0,
+                 device="cuda", dtype=torch.bfloat16):
+        self.shape, self.batch, self.ctx = shape, batch, ctx
+        s = shape
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+
+        def w(*dims, fan_in):
+            return (torch.randn(*dims, generator=g, device=device) / math.sqrt(fan_in)).to(dtype)
+
+        qkv_out = (s.num_q_heads + 2 * s.num_kv_heads) * s.head_dim
+        nq = s.num_q_heads * s.head_dim
+        # [out][in] (F.linear / addmm with a transposed view) except the
+        # gate/up weight, [in][out]
+        self.w_qkv = [w(qkv_out, s.hidden, fan_in=s.hidden) for _ in range(s.layers)]
+        self.w_o = [w(s.hidden, nq, fan_in=nq) for _ in range(s.layers)]
+        self.w_gu = [w(s.hidden, 2 * s.ffn, fan_in=s.hidden) for _ in range(s.layers)]
+        self.w_down = [w(s.hidden, s.ffn, fan_in=s.ffn) for _ in range(s.layers)]
+        self.n1 = [torch.ones(s.hidden, device=device, dtype=dtype) for _ in range(s.layers)]
+        self.n2 = [torch.ones(s.hidden, device=device, dtype=dtype) for _ in range(s.layers)]
+        # the cache of every layer: seeded random history (the layer's q is unused)
+        self.kv = [synth.make_layer(batch=batch, num_q_heads=s.num_kv_heads,
+                                    num_kv_heads=s.num_kv_heads, head_dim=s.head_dim,
+                                    dtype="bf16", ctx_lens=[ctx] * batch, seed=seed + 16 * (l + 1),
+                                    device=device)
+                   for l in range(s.layers)]
+        t = ctx - 1  # position of the token this step appends
+        self.pos = torch.full((batch,), t, dtype=torch.int32, device=device)
+        table = self.kv[0]["table"].long()
+        self.append_page = table[torch.arange(batch, device=device), t // BLOCK]
+        self.append_slot = t % BLOCK
+        self.rope_c, self.rope_s = rope_tables(self.pos, s.head_dim, s.rope_theta)
+
+    def dense(self, name: str, l: int) -> torch.Tensor:
+        """Layer l's weight `name` (qkv, o, gu, down) as an [in][out] view."""
+        w = getattr(self, "w_" + name)[l]
+        return w if name == "gu" else w.t()
+
+    def append_kv(self, l: int, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Writes the step's K and V ([B][Hkv][d]) at position ctx - 1 of every
+        sequence: K pages are [page][Hkv][128][d], V pages [page][Hkv][4][d][32]."""
+        slot = self.append_slot
+        kp, vp = self.kv[l]["k_pool"], self.kv[l]["v_pool"]
+        kp[self.append_page, :, slot, :] = k
+        vp[self.append_page, :, slot // SUBTILE, :, slot % SUBTILE] = v
+
+    def attention(self, l: int, q: torch.Tensor, policy: str, src, k: int, carried):
+        lay = self.kv[l]
+        if policy == "full":
+            out, _, _ = hylra.decode_full(q, lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"])
+            return out, carried
+        if src[l] == l:
+            idx = torch.empty(1, self.batch, self.shape.num_kv_heads, k, dtype=torch.int32,
+                              device=q.device)
+            layer = dict(lay, q=q)
+            outs, _, _ = hylra.run_policy([layer], [0], k, idx_log=idx)
+            return outs[0], idx[0]
+        out, _ = hylra.decode_sparse(q, lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
+                                     carried)
+        return out, carried
+
+    def layer(self, l: int, x: torch.Tensor, policy: str, src, k: int, carried, trace=None):
+        s = self.shape
+        B = x.shape[0]
+        x_in = x
+        F = torch.nn.functional
+        hq, hkv, d = s.num_q_heads, s.num_kv_heads, s.head_dim
+        h = F.rms_norm(x, (s.hidden,), self.n1[l], EPS)
+        qkv = F.linear(h, self.w_qkv[l])
+        # RoPE on the q and k heads together, in float32
+        qk = qkv[:, : (hq + hkv) * d].view(B, hq + hkv, d).float()
+        qk = torch.addcmul(qk * self.rope_c, qk.roll(d // 2, -1), self.rope_s).to(x.dtype)
+        q = qk[:, :hq].contiguous()
+        kk = qk[:, hq:]
+        vv = qkv[:, (hq + hkv) * d:].view(B, hkv, d)
+        self.append_kv(l, kk, vv)
+        att, carried = self.attention(l, q, policy, src, k, carried)
+        x = torch.addmm(x, att.view(B, -1).to(x.dtype), self.w_o[l].t())
+        gu = F.rms_norm(x, (s.hidden,), self.n2[l], EPS) @ self.w_gu[l]
+        x = torch.addmm(x, F.silu(gu[:, : s.ffn]) * gu[:, s.ffn:], self.w_down[l].t())
+        if trace is not None:
+            trace.append({"x": x_in, "q": q, "k": kk, "v": vv, "att": att, "idx": carried,
+                          "out": x})
+        return x, carried
+
+    def step(self, x: torch.Tensor, policy: str = "hybrid", src=None, k: int = 16, trace=None):
+        """One decode step of every layer for hidden states x [B][hidden]."""
+        carried = None
+        for l in range(self.shape.layers):
+            x, carried = self.layer(l, x, policy, src, k, carried, trace)
+        return x

@@ -40,3 +40,21 @@ def pools_from_dense(K, V, dtype=np.float32):
         vp[t // BLOCK, :, (t % BLOCK) // SUB, :, t % SUB] = V[:, t, :]
     table = np.arange(nb, dtype=np.int32)[None, :]
     return kp, vp, table
+
+
+def rope_pairs(x, pos, theta):
+    """Rotary position embedding written out pair by pair (rotate-half
+    pairing, as in Llama-3): dimensions i < d/2 and i + d/2 of every head
+    vector of sequence b are rotated by the angle pos[b] * theta^(-2i/d).
+    x is [B][H][d]; float64 result."""
+    x = np.asarray(x, np.float64)
+    B, H, d = x.shape
+    out = x.copy()
+    for b in range(B):
+        for i in range(d // 2):
+            a = float(pos[b]) * theta ** (-2.0 * i / d)
+            c, s = np.cos(a), np.sin(a)
+            x1, x2 = x[b, :, i], x[b, :, i + d // 2]
+            out[b, :, i] = x1 * c - x2 * s
+            out[b, :, i + d // 2] = x1 * s + x2 * c
+    return out
