@@ -247,6 +247,33 @@ def cpu_baseline(wl, layers, src, k, budget_s):
     n_reuse = len(src) - n_reset
     mean = lambda v: sum(v) / len(v) if v else 0.0
     step_s = n_reset * mean(t_reset) + n_reuse * mean(t_reuse)
+    # one host thread: layer 0 (a reset layer) and the first reuse layer, twice each
+    single = None
+    reuse_j = next((j for j, s in enumerate(src) if s != j), None)
+    oracle.set_threads(1)
+    try:
+        s_reset, s_reuse = [], []
+        for _ in range(2):
+            o = synth.layer_to_oracle(layers[0])
+            t0 = time.perf_counter()
+            _, _, score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
+                                             o["ctx"], num_kv_heads=wl.num_kv_heads)
+            sel, _ = oracle.topk(score, o["ctx"], k)
+            s_reset.append(time.perf_counter() - t0)
+            if reuse_j is not None:
+                o = synth.layer_to_oracle(layers[reuse_j])
+                t0 = time.perf_counter()
+                oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
+                              num_kv_heads=wl.num_kv_heads, sel=sel, k=k)
+                s_reuse.append(time.perf_counter() - t0)
+            del o
+        s_step = n_reset * mean(s_reset) + n_reuse * mean(s_reuse)
+        single = {"value": 1.0 / s_step, "unit": "steps/s", "cores": 1,
+                  "reset_layer_s": mean(s_reset), "reuse_layer_s": mean(s_reuse),
+                  "sample": "layer 0 (reset) and layer %s (reuse) timed twice each on one "
+                            "thread; same step formula" % reuse_j}
+    finally:
+        oracle.set_threads(threads)
     return {
         "value": 1.0 / step_s if step_s > 0 else None,
         "unit": "steps/s",
@@ -259,6 +286,7 @@ def cpu_baseline(wl, layers, src, k, budget_s):
                      len(t_reset), len(t_reuse), n_reset, n_reuse, time.time() - t_start),
         "reset_layer_s": mean(t_reset),
         "reuse_layer_s": mean(t_reuse),
+        "single_core": single,
     }
 
 
