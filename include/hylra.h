@@ -12,7 +12,9 @@
  * threshold theta (section 2.2).
  *
  * Conventions shared by every entry point
- *   - All device pointers are HIP device memory owned by the caller.  The
+ *   - All device pointers are HIP device memory owned by the caller (the
+ *     offloading entry points below also read K/V pools in pinned host
+ *     memory).  The
  *     library never allocates, frees, copies device-to-host or synchronises;
  *     device work is enqueued on `hip_stream` (a hipStream_t, NULL = the
  *     default stream) and is asynchronous.
@@ -131,6 +133,57 @@ hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, cons
                               float *const *out, float *const *lse, int32_t *idx_log,
                               void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Index-guided offloading (section 2.4, hardware-efficient optimisations):
+ * the indices a reuse layer carries name, before it runs, the only blocks it
+ * reads, so its KV cache can stay in host memory and just those blocks cross
+ * the host link.
+ *
+ * hylra_gather_blocks: for every (b, g, r) with n = idx[b][g][r] in
+ * [0, ceil(T_b/128)) and page = block_table[b][n] in [0, num_pages), copies
+ * the K slab [128][d] and the V slab [4][d][32] of (page, KV head g) from
+ * kv's pools into staging page b*k + r: staged_k [B*k][Hkv][128][d] and
+ * staged_v [B*k][Hkv][4][d][32], same element type.  Other staging slots
+ * are left as they are.  kv's pools may be pinned host memory that the device
+ * maps at the same address (hipHostMalloc) or device memory, over their whole
+ * extent (num_pages pages); anything else, pageable host memory included, is
+ * HYLRA_E_INVALID_ARG.  block_table, ctx_lens, idx and the staging pools are
+ * device memory.  B*k <= 2^30. */
+hylra_status hylra_gather_blocks(const hylra_shape *shape, const hylra_kv *kv, const int32_t *idx,
+                                 int32_t k, void *staged_k, void *staged_v, void *hip_stream);
+
+/* Attention over staged blocks: the result of hylra_decode_sparse on the
+ * layer's own pools with the same idx (bit for bit: the same kernel reads the
+ * same values in the same order), reading selection slot r of sequence b
+ * from staging page b*k + r as hylra_gather_blocks fills it.  ctx_lens [B]
+ * is the layer's context lengths; no block table is read. */
+hylra_status hylra_decode_staged(const hylra_shape *shape, const void *q, const void *staged_k,
+                                 const void *staged_v, const int32_t *ctx_lens, const int32_t *idx,
+                                 int32_t k, float *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream);
+
+/* hylra_run_policy with offloaded reuse layers.  offloaded (host [L]):
+ * nonzero marks a reuse layer whose kv[j] pools may be in host memory; its
+ * staging pools are staged_k[j] / staged_v[j] (host arrays of device
+ * pointers, read only for offloaded layers; each [B*k][Hkv][...] as above).
+ * A reset layer reads its whole cache and must not be offloaded
+ * (HYLRA_E_BAD_POLICY).  After each reset layer, copy_stream waits for it and
+ * then gathers the blocks of that layer's offloaded reuse layers in layer
+ * order, recording an event after each; the compute stream (hip_stream)
+ * waits for a layer's event just before that layer's attention.  The gathers
+ * thus overlap with the layers in between.  Outputs, lse and idx_log are
+ * those of hylra_run_policy.  copy_stream must differ from hip_stream when a
+ * layer is offloaded.  The events come from a per-device pool of the
+ * library (slots 0..L), so calls on one device must not run concurrently
+ * from several host threads; the sequence can be captured into a graph from
+ * hip_stream (the copy stream forks from and joins back into it). */
+hylra_status hylra_run_policy_offload(const hylra_shape *shape, int32_t num_layers,
+                                      const int32_t *src, int32_t k, const void *const *q,
+                                      const hylra_kv *kv, const uint8_t *offloaded,
+                                      void *const *staged_k, void *const *staged_v,
+                                      float *const *out, float *const *lse, int32_t *idx_log,
+                                      void *workspace, size_t workspace_bytes, void *hip_stream,
+                                      void *copy_stream);
+
 /* Offline policy dynamic program (section 2.2), host only, synchronous.
  * M: host [L][L] float32, row = target layer, column = source layer
  * (M[j*L + i] = similarity of reusing layer i's indices at layer j, i <= j;
@@ -157,6 +210,7 @@ hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
 #define HYLRA_KERNEL_FULL_ATTN 0   /* full attention layer: split pass + merge, scores, top-k */
 #define HYLRA_KERNEL_SPARSE_ATTN 1 /* selected-block attention layer: split pass + merge */
 #define HYLRA_KERNEL_TOPK 2        /* top-k of a given score array (hylra_block_topk) */
+#define HYLRA_KERNEL_GATHER 3      /* selected-block gather (hylra_gather_blocks, offloading) */
 hylra_status hylra_timer_start(int32_t kind, int32_t capacity);
 hylra_status hylra_timer_stop(int32_t kind, double *total_ms, int32_t *launches);
 

@@ -184,18 +184,80 @@ hylra_status run_full(const hylra_shape *s, const void *q, const hylra_kv *kv, f
 }
 
 // Reuse layer: one launch -- attention over the selected blocks and merge.
+// staged: kv holds staging pools (selection slot r of sequence b in page
+// b * k + r) instead of the layer's pools and block table.
 hylra_status run_sparse(const hylra_shape *s, const void *q, const hylra_kv *kv,
                         const int32_t *idx, int k, float *out, float *lse, int32_t *log,
-                        const Workspace &w, void *stream) {
+                        const Workspace &w, void *stream, bool staged = false) {
   const hylra::SplitPlan plan =
       hylra::plan_sparse(s->batch, s->num_kv_heads, s->max_blocks_per_seq, k,
                          s->num_q_heads / s->num_kv_heads, s->head_dim);
   hylra::AttnArgs a = attn_args(s, q, kv, idx, k, plan, w);
+  a.staged = staged ? 1 : 0;
   a.out = out;
   a.lse = lse;
   a.sel_log = log;
   return device_status(hylra::launch_attn(a, s->dtype, s->head_dim, s->batch, stream),
                        "attention launch");
+}
+
+size_t elt_bytes(const hylra_shape *s) { return s->dtype == HYLRA_BF16 ? 2 : 4; }
+
+// Gather of the selected blocks of one layer into staging pools.
+hylra_status run_gather(const hylra_shape *s, const hylra_kv *kv, const int32_t *idx, int k,
+                        void *dst_k, void *dst_v, void *stream) {
+  hylra::GatherArgs g{};
+  g.k_src = static_cast<const char *>(kv->k_pool);
+  g.v_src = static_cast<const char *>(kv->v_pool);
+  g.num_pages = kv->num_pages;
+  g.table = kv->block_table;
+  g.ctx = kv->ctx_lens;
+  g.idx = idx;
+  g.k = k;
+  g.max_blocks = s->max_blocks_per_seq;
+  g.num_kv_heads = s->num_kv_heads;
+  g.tile_bytes = (int)(hylra::kBlockTokens * s->head_dim * elt_bytes(s));
+  g.k_dst = static_cast<char *>(dst_k);
+  g.v_dst = static_cast<char *>(dst_v);
+  return device_status(hylra::launch_gather(g, s->batch, stream), "gather launch");
+}
+
+// A staging-pool view for the attention kernel: the block table is not read.
+hylra_kv staged_kv(const hylra_shape *s, const void *k_pool, const void *v_pool, int k,
+                   const int32_t *ctx_lens) {
+  hylra_kv v{};
+  v.k_pool = k_pool;
+  v.v_pool = v_pool;
+  v.num_pages = (int64_t)s->batch * k;
+  v.block_table = nullptr;
+  v.ctx_lens = ctx_lens;
+  return v;
+}
+
+// The gather reads the source pools through the addresses the caller passes:
+// both pools must be device memory or pinned host memory mapped at the same
+// address over their whole extent (num_pages pages).
+hylra_status check_gather_source(const hylra_shape *s, const hylra_kv *kv) {
+  const size_t bytes = (size_t)kv->num_pages * s->num_kv_heads * hylra::kBlockTokens *
+                       s->head_dim * elt_bytes(s);
+  for (const void *p : {kv->k_pool, kv->v_pool}) {
+    int readable = 0;
+    if (hylra_status st = device_status(hylra::pool_readable(p, bytes, &readable), "pointer query"))
+      return st;
+    if (!readable)
+      return fail(HYLRA_E_INVALID_ARG,
+                  "K/V pools to gather from must be device memory or pinned host memory "
+                  "(hipHostMalloc) the device maps at the same address, over %zu bytes", bytes);
+  }
+  return HYLRA_OK;
+}
+
+hylra_status check_staging(const void *k_pool, const void *v_pool) {
+  if (k_pool == nullptr || v_pool == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "staging pools must be non-NULL");
+  if (!aligned16(k_pool) || !aligned16(v_pool))
+    return fail(HYLRA_E_INVALID_ARG, "staging pools must be 16-byte aligned");
+  return HYLRA_OK;
 }
 
 }  // namespace
@@ -335,6 +397,131 @@ hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, cons
       const int32_t *carried = idx_log ? idx_log + (size_t)src[j] * row : w.idx;
       int32_t *log = idx_log ? idx_log + (size_t)j * row : nullptr;
       st = run_sparse(shape, q[j], &kv[j], carried, k, out[j], lj, log, w, hip_stream);
+    }
+    if (st) return fail(st, "layer %d: %s", j, hylra_last_error());
+  }
+  return ok();
+}
+
+hylra_status hylra_gather_blocks(const hylra_shape *shape, const hylra_kv *kv, const int32_t *idx,
+                                 int32_t k, void *staged_k, void *staged_v, void *hip_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (hylra_status st = check_kv(kv)) return st;
+  if (idx == nullptr) return fail(HYLRA_E_INVALID_ARG, "idx must be non-NULL");
+  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if ((long)shape->batch * k > (1L << 30))
+    return fail(HYLRA_E_UNSUPPORTED, "batch * k = %ld exceeds 2^30 staging pages", (long)shape->batch * k);
+  if (hylra_status st = check_staging(staged_k, staged_v)) return st;
+  if (hylra_status st = check_gather_source(shape, kv)) return st;
+  if (hylra_status st = run_gather(shape, kv, idx, k, staged_k, staged_v, hip_stream)) return st;
+  return ok();
+}
+
+hylra_status hylra_decode_staged(const hylra_shape *shape, const void *q, const void *staged_k,
+                                 const void *staged_v, const int32_t *ctx_lens, const int32_t *idx,
+                                 int32_t k, float *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (hylra_status st = check_staging(staged_k, staged_v)) return st;
+  if (q == nullptr || out == nullptr || idx == nullptr || ctx_lens == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "q, ctx_lens, idx and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(HYLRA_E_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if ((long)shape->batch * k > (1L << 30))
+    return fail(HYLRA_E_UNSUPPORTED, "batch * k = %ld exceeds 2^30 staging pages", (long)shape->batch * k);
+  Workspace w;
+  if (hylra_status st = check_ws(shape, k, workspace, workspace_bytes, w)) return st;
+  const hylra_kv kv = staged_kv(shape, staged_k, staged_v, k, ctx_lens);
+  if (hylra_status st = run_sparse(shape, q, &kv, idx, k, out, lse, nullptr, w, hip_stream, true))
+    return st;
+  return ok();
+}
+
+hylra_status hylra_run_policy_offload(const hylra_shape *shape, int32_t num_layers,
+                                      const int32_t *src, int32_t k, const void *const *q,
+                                      const hylra_kv *kv, const uint8_t *offloaded,
+                                      void *const *staged_k, void *const *staged_v,
+                                      float *const *out, float *const *lse, int32_t *idx_log,
+                                      void *workspace, size_t workspace_bytes, void *hip_stream,
+                                      void *copy_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (num_layers < 1) return fail(HYLRA_E_INVALID_ARG, "num_layers must be >= 1");
+  if (src == nullptr || q == nullptr || kv == nullptr || out == nullptr || offloaded == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "src, q, kv, offloaded and out must be non-NULL");
+  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if ((long)shape->batch * k > (1L << 30))
+    return fail(HYLRA_E_UNSUPPORTED, "batch * k = %ld exceeds 2^30 staging pages", (long)shape->batch * k);
+  if (src[0] != 0) return fail(HYLRA_E_BAD_POLICY, "layer 0 must reset (src[0] = %d)", src[0]);
+  for (int j = 1; j < num_layers; ++j)
+    if (src[j] != j && src[j] != src[j - 1])
+      return fail(HYLRA_E_BAD_POLICY, "src[%d] = %d is neither %d nor src[%d] = %d", j, src[j], j,
+                  j - 1, src[j - 1]);
+  bool any = false;
+  for (int j = 0; j < num_layers; ++j) any = any || offloaded[j];
+  if (any && copy_stream == hip_stream)
+    return fail(HYLRA_E_INVALID_ARG, "copy_stream must differ from hip_stream");
+  for (int j = 0; j < num_layers; ++j) {
+    if (hylra_status st = check_kv(&kv[j])) return fail(st, "layer %d: %s", j, hylra_last_error());
+    if (q[j] == nullptr || out[j] == nullptr || !aligned16(q[j]) || !aligned16(out[j]))
+      return fail(HYLRA_E_INVALID_ARG, "layer %d: q and out must be non-NULL and 16-byte aligned", j);
+    if (offloaded[j]) {
+      if (src[j] == j)
+        return fail(HYLRA_E_BAD_POLICY,
+                    "layer %d resets and needs its whole KV cache on the device; only reuse "
+                    "layers may be offloaded", j);
+      if (staged_k == nullptr || staged_v == nullptr)
+        return fail(HYLRA_E_INVALID_ARG, "staged_k and staged_v must be non-NULL");
+      if (hylra_status st = check_staging(staged_k[j], staged_v[j]))
+        return fail(st, "layer %d: %s", j, hylra_last_error());
+      if (hylra_status st = check_gather_source(shape, &kv[j]))
+        return fail(st, "layer %d: %s", j, hylra_last_error());
+    }
+  }
+  Workspace w;
+  if (hylra_status st = check_ws(shape, k, workspace, workspace_bytes, w)) return st;
+  const size_t row = (size_t)shape->batch * shape->num_kv_heads * k;
+  // event slots: slot j marks the end of layer j's gather on the copy
+  // stream; slot num_layers marks the index set of the latest reset
+  const int fork_slot = num_layers;
+  for (int j = 0; j < num_layers; ++j) {
+    float *lj = lse ? lse[j] : nullptr;
+    hylra_status st;
+    if (src[j] == j) {
+      bool gathers = false;
+      for (int i = j + 1; i < num_layers && src[i] == j; ++i) gathers = gathers || offloaded[i];
+      const bool used = idx_log != nullptr || (j + 1 < num_layers && src[j + 1] == j);
+      int32_t *dst = used ? (idx_log ? idx_log + (size_t)j * row : w.idx) : nullptr;
+      st = run_full(shape, q[j], &kv[j], out[j], lj, nullptr, dst, k, w, hip_stream);
+      if (st) return fail(st, "layer %d: %s", j, hylra_last_error());
+      if (gathers) {
+        // fork: once the index set exists, the copy stream brings in every
+        // offloaded reuse layer's blocks, in layer order, while the compute
+        // stream runs the layers in between
+        if (hylra_status e = device_status(hylra::event_record(hip_stream, fork_slot), "event record"))
+          return e;
+        if (hylra_status e = device_status(hylra::event_wait(copy_stream, fork_slot), "event wait"))
+          return e;
+        for (int i = j + 1; i < num_layers && src[i] == j; ++i) {
+          if (!offloaded[i]) continue;
+          st = run_gather(shape, &kv[i], dst, k, staged_k[i], staged_v[i], copy_stream);
+          if (st) return fail(st, "layer %d gather: %s", i, hylra_last_error());
+          if (hylra_status e = device_status(hylra::event_record(copy_stream, i), "event record"))
+            return e;
+        }
+      }
+    } else {
+      const int32_t *carried = idx_log ? idx_log + (size_t)src[j] * row : w.idx;
+      int32_t *log = idx_log ? idx_log + (size_t)j * row : nullptr;
+      if (offloaded[j]) {
+        // join: this layer's staged blocks are complete.  The next reset,
+        // which overwrites the carried set, runs after every reuse layer of
+        // this source, so after all of the gathers that read the set.
+        if (hylra_status e = device_status(hylra::event_wait(hip_stream, j), "event wait")) return e;
+        const hylra_kv skv = staged_kv(shape, staged_k[j], staged_v[j], k, kv[j].ctx_lens);
+        st = run_sparse(shape, q[j], &skv, carried, k, out[j], lj, log, w, hip_stream, true);
+      } else {
+        st = run_sparse(shape, q[j], &kv[j], carried, k, out[j], lj, log, w, hip_stream);
+      }
     }
     if (st) return fail(st, "layer %d: %s", j, hylra_last_error());
   }

@@ -36,6 +36,8 @@ struct AttnArgs {
   const int32_t *table;
   const int32_t *ctx;
   const int32_t *sel;  // nullptr: every block (full); else [B][Hkv][k] block ids
+  int staged;          // sparse mode: selection slot r of sequence b sits in page b * k + r
+                       // of a staging pool (table not read)
   int k;
   int max_blocks;
   int num_q_heads;
@@ -68,8 +70,30 @@ struct TopkArgs {
   int k;
 };
 
+// Index-guided gather (hylra_offload.hip): the K and V tiles of the selected
+// blocks, (page, KV head) slabs of tile_bytes each, copied from pools the
+// device can read (host or device memory) into staging pools
+// [B * k][Hkv][...] at page b * k + r.
+struct GatherArgs {
+  const char *k_src, *v_src;
+  int64_t num_pages;
+  const int32_t *table, *ctx, *idx;
+  int k, max_blocks, num_kv_heads, tile_bytes;
+  char *k_dst, *v_dst;
+};
+
 // Launchers: return 0 on success or the hipError_t code of the launch.
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream);
+int launch_gather(const GatherArgs &a, int batch, void *stream);
+// Cross-stream ordering through a per-device pool of events: event_record
+// records event `slot` on `stream` (after the work enqueued so far),
+// event_wait makes `stream` wait for the last recording of `slot`.
+int event_record(void *stream, int slot);
+// Sets *readable to 1 when both the first and the last byte of [base,
+// base + bytes) are device memory or pinned host memory that the device maps
+// at the same address (what the gather kernel dereferences), else 0.
+int pool_readable(const void *base, size_t bytes, int *readable);
+int event_wait(void *stream, int slot);
 int launch_topk(const TopkArgs &a, int batch, void *stream);
 int launch_read_probe(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
 
@@ -84,8 +108,17 @@ int launch_overlap(const OverlapArgs &a, void *stream);
 const char *device_error_string(int code);
 
 // Kernel timers (see hylra_timer_start in hylra.h).
-enum TimerKind { kTimerFullAttn = 0, kTimerSparseAttn = 1, kTimerTopk = 2, kNumTimers = 3 };
+enum TimerKind {
+  kTimerFullAttn = 0,
+  kTimerSparseAttn = 1,
+  kTimerTopk = 2,
+  kTimerGather = 3,
+  kNumTimers = 4
+};
 int timer_start(int kind, int capacity);
 int timer_stop(int kind, double *total_ms, int *launches);
+// The event pair of the next timed launch of `kind` (both NULL when the timer
+// is not running or full); the launch records them (hipExtLaunchKernel).
+void timer_take(int kind, void **start, void **stop);
 
 }  // namespace hylra

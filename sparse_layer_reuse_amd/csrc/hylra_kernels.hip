@@ -110,7 +110,8 @@ __device__ __forceinline__ bool resolve_chunk(const AttnArgs &a, int b, int g, i
   valid = T - (n * kBlockTokens + sub * kChunkTokens);
   if (valid <= 0) return false;
   if (valid > kChunkTokens) valid = kChunkTokens;
-  page = scalar_load(a.table, (int64_t)b * a.max_blocks + n);
+  page = a.staged ? b * a.k + pos / kChunksPerBlock
+                  : scalar_load(a.table, (int64_t)b * a.max_blocks + n);
   return page >= 0 && page < a.num_pages;
 }
 
@@ -1085,6 +1086,12 @@ struct TimerScope {
 };
 
 }  // namespace
+
+void timer_take(int kind, void **start, void **stop) {
+  const TimerScope tm(kind);
+  *start = tm.start;
+  *stop = tm.stop;
+}
 
 int timer_start(int kind, int capacity) {
   KernelTimer &t = g_timers[kind];

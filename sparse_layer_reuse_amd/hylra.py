@@ -62,6 +62,9 @@ def _load():
         "hylra_timer_stop": [I32, P, P],
         "hylra_read_probe": [P, SZ, P, P],
         "hylra_overlap_matrix": [I32, I32, I32, I32, P, P, P],
+        "hylra_gather_blocks": [SP, KP, P, I32, P, P, P],
+        "hylra_decode_staged": [SP, P, P, P, P, P, I32, P, P, P, SZ, P],
+        "hylra_run_policy_offload": [SP, I32, P, I32, P, KP, P, P, P, P, P, P, P, SZ, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -78,12 +81,13 @@ _lib = _load()
 
 EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
             "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_timer_start",
-            "hylra_timer_stop", "hylra_overlap_matrix", "hylra_read_probe", "hylra_status_str",
+            "hylra_timer_stop", "hylra_overlap_matrix", "hylra_read_probe", "hylra_gather_blocks",
+            "hylra_decode_staged", "hylra_run_policy_offload", "hylra_status_str",
             "hylra_last_error")
 
-KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_TOPK = range(3)
+KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_TOPK, KERNEL_GATHER = range(4)
 KERNEL_NAMES = {KERNEL_FULL_ATTN: "attn_full_layer", KERNEL_SPARSE_ATTN: "attn_sparse_layer",
-                KERNEL_TOPK: "score_topk"}
+                KERNEL_TOPK: "score_topk", KERNEL_GATHER: "gather_blocks"}
 
 
 def _status_str(st: int) -> str:
@@ -149,9 +153,17 @@ def check_pool_shapes(k_shape, v_shape):
                          "(got %s and %s)" % (k_shape, v_shape))
 
 
-def make_kv(k_pool, v_pool, table, ctx) -> KV:
-    _need(k_pool, "k_pool", tuple(_DTYPES), 4)
-    _need(v_pool, "v_pool", k_pool.dtype, 5)
+def _need_pool(t, name, dtype, ndim, host_ok):
+    """A pool on the GPU, or (host_ok) in pinned host memory the GPU can read."""
+    host = host_ok and isinstance(t, torch.Tensor) and not t.is_cuda
+    if host and not t.is_pinned():
+        raise ValueError("%s in host memory must be pinned (pin_memory=True)" % name)
+    _need(t, name, dtype, ndim, cuda=not host)
+
+
+def make_kv(k_pool, v_pool, table, ctx, *, host_ok=False) -> KV:
+    _need_pool(k_pool, "k_pool", tuple(_DTYPES), 4, host_ok)
+    _need_pool(v_pool, "v_pool", k_pool.dtype, 5, host_ok)
     _need(table, "block_table", torch.int32, 2)
     _need(ctx, "ctx_lens", torch.int32, 1)
     check_pool_shapes(k_pool.shape, v_pool.shape)
@@ -231,12 +243,66 @@ def decode_sparse(q, k_pool, v_pool, table, ctx, idx, *, scale=0.0, out=None, ls
     return out, lse
 
 
+def staging_pools(k_pool, batch: int, k: int, device="cuda"):
+    """Device staging pools for the selected blocks of one layer:
+    K [B*k][Hkv][128][d] and V [B*k][Hkv][4][d][32]."""
+    _, Hkv, _, d = k_pool.shape
+    sk = torch.empty(batch * k, Hkv, BLOCK, d, dtype=k_pool.dtype, device=device)
+    sv = torch.empty(batch * k, Hkv, BLOCK // SUBTILE, d, SUBTILE, dtype=k_pool.dtype, device=device)
+    return sk, sv
+
+
+def _check_staging(staged_k, staged_v, k_dtype, batch, k, Hkv, d):
+    _need(staged_k, "staged_k", k_dtype, 4)
+    _need(staged_v, "staged_v", k_dtype, 5)
+    check_pool_shapes(staged_k.shape, staged_v.shape)
+    if tuple(staged_k.shape) != (batch * k, Hkv, BLOCK, d):
+        raise ValueError("staging pools must hold B*k = %d pages of %d KV heads, d = %d (got %s)"
+                         % (batch * k, Hkv, d, tuple(staged_k.shape)))
+
+
+def gather_blocks(k_pool, v_pool, table, ctx, idx, staged_k, staged_v, *, stream=None):
+    """Copies the selected blocks idx [B][Hkv][k] of a layer (pools on the GPU
+    or pinned in host memory) into staging pools (see staging_pools)."""
+    kv = make_kv(k_pool, v_pool, table, ctx, host_ok=True)
+    _need(idx, "idx", torch.int32, 3)
+    B, Hkv, k = idx.shape
+    _check_staging(staged_k, staged_v, k_pool.dtype, B, k, Hkv, k_pool.shape[3])
+    if table.shape[0] != B or k_pool.shape[1] != Hkv:
+        raise ValueError("idx, block_table and the pools disagree on the batch or KV heads")
+    shape = Shape(B, Hkv, Hkv, k_pool.shape[3], BLOCK, _DTYPES[k_pool.dtype], table.shape[1], 0.0)
+    _check(_lib.hylra_gather_blocks(ctypes.byref(shape), ctypes.byref(kv), _ptr(idx), int(k),
+                                    _ptr(staged_k), _ptr(staged_v), _stream(stream)))
+
+
+def decode_staged(q, staged_k, staged_v, ctx, idx, max_blocks: int, *, scale=0.0, out=None,
+                  lse=None, ws=None, stream=None):
+    """Attention over staged blocks: the result of decode_sparse on the
+    layer's own pools with the same idx.  max_blocks is the layer's block-table
+    row length.  Returns (out, lse)."""
+    _need(q, "q", tuple(_DTYPES), 3)
+    _need(idx, "idx", torch.int32, 3)
+    _need(ctx, "ctx_lens", torch.int32, 1)
+    B, Hq, d = q.shape
+    k = idx.shape[2]
+    Hkv = staged_k.shape[1]
+    _check_staging(staged_k, staged_v, q.dtype, B, k, Hkv, d)
+    shape = Shape(B, Hq, Hkv, d, BLOCK, _DTYPES[q.dtype], int(max_blocks), float(scale))
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device) if out is None else out
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if lse is None else lse
+    ws = workspace(shape, k, q.device) if ws is None else ws
+    _check(_lib.hylra_decode_staged(ctypes.byref(shape), _ptr(q), _ptr(staged_k), _ptr(staged_v),
+                                    _ptr(ctx), _ptr(idx), int(k), _ptr(out), _ptr(lse), _ptr(ws),
+                                    ws.numel(), _stream(stream)))
+    return out, lse
+
+
 class PolicyPlan:
     """Pre-marshalled arguments of hylra_run_policy for a fixed set of layer
     tensors, so that repeated decode steps pay no Python marshalling."""
 
     def __init__(self, layers: Sequence[dict], src: Sequence[int], k: int, *, scale=0.0,
-                 outs=None, lses=None, idx_log=None, ws=None):
+                 outs=None, lses=None, idx_log=None, ws=None, host_ok=None):
         first = layers[0]
         self.shape = make_shape(first["q"], first["k_pool"], first["table"], scale)
         L = len(layers)
@@ -245,8 +311,9 @@ class PolicyPlan:
         B, Hq, d = first["q"].shape
         dev = first["q"].device
         self.src = (ctypes.c_int32 * L)(*[int(s) for s in src])
-        self.kvs = (KV * L)(*[make_kv(l["k_pool"], l["v_pool"], l["table"], l["ctx"])
-                              for l in layers])
+        host_ok = host_ok if host_ok is not None else [False] * L
+        self.kvs = (KV * L)(*[make_kv(l["k_pool"], l["v_pool"], l["table"], l["ctx"],
+                                      host_ok=bool(h)) for l, h in zip(layers, host_ok)])
         for l in layers:
             _need(l["q"], "q", first["q"].dtype, 3)
         self.qs = (ctypes.c_void_p * L)(*[l["q"].data_ptr() for l in layers])
@@ -265,6 +332,42 @@ class PolicyPlan:
                                      self.qs, self.kvs, self.outs, self.lses,
                                      _ptr(self.idx_log), _ptr(self.ws), self.ws.numel(),
                                      _stream(stream)))
+        return self.out, self.lse
+
+
+class OffloadPlan(PolicyPlan):
+    """Pre-marshalled arguments of hylra_run_policy_offload: layers whose
+    entry in `offloaded` is true are reuse layers whose pools may be pinned
+    host tensors; each gets device staging pools."""
+
+    def __init__(self, layers: Sequence[dict], src: Sequence[int], k: int, offloaded, *,
+                 scale=0.0, outs=None, lses=None, idx_log=None, ws=None, staging=None):
+        L = len(layers)
+        if len(offloaded) != L:
+            raise ValueError("offloaded needs one entry per layer")
+        super().__init__(layers, src, k, scale=scale, outs=outs, lses=lses, idx_log=idx_log,
+                         ws=ws, host_ok=[bool(o) for o in offloaded])
+        B = layers[0]["q"].shape[0]
+        self.offloaded = (ctypes.c_uint8 * L)(*[1 if o else 0 for o in offloaded])
+        self.staging = staging if staging is not None else [
+            staging_pools(l["k_pool"], B, self.k) if off else (None, None)
+            for l, off in zip(layers, offloaded)]
+        for (sk, sv), l, off in zip(self.staging, layers, offloaded):
+            if off:
+                _check_staging(sk, sv, l["k_pool"].dtype, B, self.k, l["k_pool"].shape[1],
+                               l["k_pool"].shape[3])
+        self.sks = (ctypes.c_void_p * L)(*[sk.data_ptr() if sk is not None else 0
+                                           for sk, _ in self.staging])
+        self.svs = (ctypes.c_void_p * L)(*[sv.data_ptr() if sv is not None else 0
+                                           for _, sv in self.staging])
+
+    def run(self, stream=None, copy_stream=None):
+        if copy_stream is None:
+            raise ValueError("run needs a copy stream distinct from the compute stream")
+        _check(_lib.hylra_run_policy_offload(
+            ctypes.byref(self.shape), self.L, self.src, self.k, self.qs, self.kvs,
+            self.offloaded, self.sks, self.svs, self.outs, self.lses, _ptr(self.idx_log),
+            _ptr(self.ws), self.ws.numel(), _stream(stream), _stream(copy_stream)))
         return self.out, self.lse
 
 

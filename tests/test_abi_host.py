@@ -229,3 +229,68 @@ def test_overlap_matrix_argument_checks():
     assert lib.hylra_overlap_matrix(1, 4, 2, 0, ok_ptr, ok_ptr, None) == H.E_INVALID_ARG
     assert lib.hylra_overlap_matrix(1, 4, 2, 8, ok_ptr + 2, ok_ptr, None) == H.E_INVALID_ARG
     assert lib.hylra_overlap_matrix(1, 1024, 2, 64, ok_ptr, ok_ptr, None) == H.E_UNSUPPORTED
+
+
+def _offload(src, offloaded, k=4, staged=True, staged_ptr=0x60000, copy=ctypes.c_void_p(0x7000)):
+    L = len(src)
+    s = _shape()
+    srcs = (ctypes.c_int32 * L)(*src)
+    kvs = (H.KV * L)(*[_kv() for _ in range(L)])
+    qs = (ctypes.c_void_p * L)(*([0x10000] * L))
+    outs = (ctypes.c_void_p * L)(*([0x50000] * L))
+    offl = None if offloaded is None else (ctypes.c_uint8 * L)(*offloaded)
+    sk = (ctypes.c_void_p * L)(*([staged_ptr] * L)) if staged else None
+    return H._lib.hylra_run_policy_offload(ctypes.byref(s), L, srcs, k, qs, kvs, offl, sk, sk,
+                                           outs, None, None, FAKE, 1 << 30, None, copy)
+
+
+def test_offload_argument_checks():
+    # every case fails on the host before anything is enqueued
+    assert _offload([0, 0, 2], [0, 0, 1]) == H.E_BAD_POLICY  # an offloaded reset layer
+    assert "reset" in H.last_error()
+    assert _offload([0, 0], [1, 0]) == H.E_BAD_POLICY
+    assert _offload([0, 2], [0, 1]) == H.E_BAD_POLICY  # malformed source list
+    assert _offload([0, 0], [0, 1], copy=None) == H.E_INVALID_ARG  # copy stream == compute stream
+    assert "copy_stream" in H.last_error()
+    assert _offload([0, 0], [0, 1]) == H.E_INVALID_ARG  # pools the device cannot read
+    assert _offload([0, 0], [0, 1], staged=False) == H.E_INVALID_ARG
+    assert _offload([0, 0], [0, 1], staged_ptr=0x60008) == H.E_INVALID_ARG  # misaligned
+    assert _offload([0, 0], [0, 1], k=0) == H.E_INVALID_ARG
+    assert _offload([0, 0], None) == H.E_INVALID_ARG
+
+
+def test_gather_and_staged_argument_checks():
+    lib, s, kv = H._lib, _shape(), _kv()
+    g = lambda idx=FAKE, k=4, sk=FAKE, sv=FAKE, kv=kv: lib.hylra_gather_blocks(
+        ctypes.byref(s), ctypes.byref(kv), idx, k, sk, sv, None)
+    assert g(idx=None) == H.E_INVALID_ARG
+    assert g(k=0) == H.E_INVALID_ARG
+    assert g(sk=None) == H.E_INVALID_ARG
+    assert g(sv=ctypes.c_void_p(0x10008)) == H.E_INVALID_ARG
+    assert g(kv=_kv(block_table=None)) == H.E_INVALID_ARG
+    assert g(k=1 << 30) == H.E_UNSUPPORTED  # B * k staging pages
+    d = lambda q=FAKE, ctx=FAKE, idx=FAKE, k=4, out=FAKE, sk=FAKE, ws_bytes=1 << 30: \
+        lib.hylra_decode_staged(ctypes.byref(s), q, sk, FAKE, ctx, idx, k, out, None, FAKE,
+                                ws_bytes, None)
+    assert d(q=None) == H.E_INVALID_ARG
+    assert d(ctx=None) == H.E_INVALID_ARG
+    assert d(idx=None) == H.E_INVALID_ARG
+    assert d(out=None) == H.E_INVALID_ARG
+    assert d(k=0) == H.E_INVALID_ARG
+    assert d(sk=None) == H.E_INVALID_ARG
+    assert d(ws_bytes=16) == H.E_WORKSPACE
+
+
+def test_binding_offload_checks():
+    import torch
+    k_pool = torch.zeros(4, 2, 128, 64)
+    v_pool = torch.zeros(4, 2, 4, 64, 32)
+    table = torch.zeros(1, 4, dtype=torch.int32)
+    ctx = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="pinned"):
+        H.make_kv(k_pool, v_pool, table, ctx, host_ok=True)
+    with pytest.raises(ValueError, match="GPU"):
+        H.make_kv(k_pool, v_pool, table, ctx)
+    with pytest.raises((ValueError, TypeError)):
+        H._check_staging(torch.zeros(3, 2, 128, 64), torch.zeros(3, 2, 4, 64, 32), torch.float32,
+                         1, 4, 2, 64)

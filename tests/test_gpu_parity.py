@@ -224,12 +224,15 @@ def sampled_sequences(layer, seqs):
             "ctx": layer["ctx"][bs]}
 
 
-def check_policy_run(H, layers_gpu, src, k, dtype, num_kv_heads, check_layers=None, seqs=None):
+def check_policy_run(H, layers_gpu, src, k, dtype, num_kv_heads, check_layers=None, seqs=None,
+                     run=None):
     """Run the GPU policy and compare the chosen layers (and, with ``seqs``,
-    only those sequences) with the oracle."""
+    only those sequences) with the oracle.  ``run(outs, lses)`` replaces the
+    default hylra.run_policy call; it returns (outs, lses, idx_log)."""
     bufs = [nan_out(l["q"]) for l in layers_gpu]
-    outs, lses, idx_log = H.run_policy(layers_gpu, src, k, outs=[b[0] for b in bufs],
-                                       lses=[b[1] for b in bufs])
+    if run is None:
+        run = lambda outs, lses: H.run_policy(layers_gpu, src, k, outs=outs, lses=lses)
+    outs, lses, idx_log = run([b[0] for b in bufs], [b[1] for b in bufs])
     first = layers_gpu[0]
     assert counters_are_zero(H, first["q"], first["k_pool"], first["table"], k)
     idx_gpu = idx_log.cpu().numpy()

@@ -19,7 +19,7 @@ from sparse_layer_reuse_amd import build as B
 SRC = os.path.join(B.CSRC, "hylra_kernels.hip")
 
 
-def resource_report(tmp_path):
+def resource_report(tmp_path, src=SRC):
     try:
         hipcc = B.hipcc()
     except RuntimeError:
@@ -28,7 +28,7 @@ def resource_report(tmp_path):
         pytest.skip("hipcc not available")
     cmd = [hipcc, "--offload-arch=" + B.ARCH, "-O3", "-std=c++17", "-fPIC", "-c",
            "-I" + os.path.join(B.ROOT, "include"), *B.DEVICE_FLAGS,
-           "-Rpass-analysis=kernel-resource-usage", SRC, "-o", str(tmp_path / "k.o")]
+           "-Rpass-analysis=kernel-resource-usage", src, "-o", str(tmp_path / "k.o")]
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=B.COMPILE_TIMEOUT_S)
     assert res.returncode == 0, res.stderr[-2000:]
     kernels, cur = {}, None
@@ -55,3 +55,10 @@ def test_attention_kernels_fit_without_scratch(tmp_path):
         assert r["Occupancy"] >= 2, (name, r)
     topk = [v for k, v in kernels.items() if "score_topk" in k]
     assert topk and topk[0]["ScratchSize"] == 0
+
+
+def test_gather_kernel_has_no_scratch(tmp_path):
+    kernels = resource_report(tmp_path, os.path.join(B.CSRC, "hylra_offload.hip"))
+    gather = [v for k, v in kernels.items() if "gather_blocks" in k]
+    assert len(gather) == 1, sorted(kernels)
+    assert gather[0]["ScratchSize"] == 0, gather[0]
