@@ -55,6 +55,10 @@ def parse():
                    help="time a whole random-weight Llama-3-8B-shaped decode step (projections, "
                         "RoPE, KV append, attention, MLP) for the hybrid and the full policy "
                         "instead of attention alone")
+    p.add_argument("--offload", action="store_true",
+                   help="index-guided offloading: the reuse layers' KV caches in pinned host "
+                        "memory, their selected blocks gathered on a copy stream (with --e2e: "
+                        "the end-to-end step as well)")
     p.add_argument("--profiled", action="store_true",
                    help="policy from the DP on a similarity matrix profiled on the GPU "
                         "(all-reset step, logged top-k overlaps) instead of the synthetic one")
@@ -306,6 +310,23 @@ def e2e(args, wl, k, src, policy_desc):
     x = torch.randn(wl.batch, shape.hidden, generator=g, device="cuda").to(torch.bfloat16)
     ms_h, _ = graph_timed(lambda: dec.step(x, "hybrid", src, k), args.steps, args.warmup, torch)
     ms_f, _ = graph_timed(lambda: dec.step(x, "full", src, k), args.steps, args.warmup, torch)
+    extra = {}
+    if args.offload:
+        reuse = [j for j, s in enumerate(src) if s != j]
+        dec.offload(reuse)
+        ms_o, _ = graph_timed(lambda: dec.step(x, "hybrid", src, k), args.steps, args.warmup, torch)
+        elt = 2
+        kv_layer = 2 * wl.batch * wl.num_kv_heads * wl.blocks * 128 * wl.head_dim * elt
+        extra = {"offload": {
+            "offloaded_layers": len(reuse),
+            "hybrid_offload_ms_per_step": ms_o,
+            "hybrid_offload_steps_per_s": 1000.0 / ms_o,
+            "offload_over_device": ms_o / ms_h,
+            "kv_bytes_in_host_memory": kv_layer * len(reuse),
+            "kv_bytes_on_device": kv_layer * (len(src) - len(reuse)),
+            "host_link_bytes_per_step": len(reuse) * 2 * wl.batch * wl.num_kv_heads
+                                        * min(k, wl.blocks) * 128 * wl.head_dim * elt,
+        }}
     return {
         "metric": "end-to-end decode steps/s, random-weight Llama-3-shaped model, hybrid vs full",
         "value": 1000.0 / ms_h, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
@@ -318,6 +339,82 @@ def e2e(args, wl, k, src, policy_desc):
         "hybrid_over_full": ms_f / ms_h,
         "pages_context": {"speedup_vs_full_attention": 1.45, "scope": "end-to-end LLM decode",
                           "sequence_length": 60000, "hardware": "not stated"},
+        **extra,
+    }
+
+
+def link_ceiling(torch, mib=1024, reps=3):
+    """Pinned host -> device copy rate (copy engine) of `mib` MiB: the
+    practical ceiling of the host link, in GB/s."""
+    src = torch.empty(mib << 20, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, (mib << 20) / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+def offload_bench(args, wl, k, src, policy_desc, layers, torch, hylra):
+    """Attention-only step with the reuse layers' caches in pinned host
+    memory, against the same step with every cache on the device."""
+    L = len(src)
+    reuse = [j for j, s in enumerate(src) if s != j]
+    offloaded = [s != j for j, s in enumerate(src)]
+    device_plan = hylra.PolicyPlan(layers, src, k)
+    ms_dev, g = graph_timed(device_plan.run, args.steps, args.warmup, torch)
+    del g, device_plan
+    host_layers = []
+    for j, lay in enumerate(layers):
+        if offloaded[j]:
+            lay = dict(lay, k_pool=lay["k_pool"].cpu().pin_memory(),
+                       v_pool=lay["v_pool"].cpu().pin_memory())
+        host_layers.append(lay)
+    del layers
+    torch.cuda.empty_cache()
+    copy = torch.cuda.Stream()
+    plan = hylra.OffloadPlan(host_layers, src, k, offloaded)
+    # eager steps with the gather and attention kernels timed
+    kinds = (hylra.KERNEL_GATHER, hylra.KERNEL_SPARSE_ATTN, hylra.KERNEL_FULL_ATTN)
+    ms_eager, kern = timed(lambda: plan.run(copy_stream=copy), args.steps, args.warmup, torch,
+                           kinds, hylra)
+    ms_off, g = graph_timed(lambda: plan.run(copy_stream=copy), args.steps, args.warmup, torch)
+    del g
+    B, Hkv, d = wl.batch, wl.num_kv_heads, wl.head_dim
+    elt = 4 if wl.dtype == "f32" else 2
+    per_gather = 2 * B * Hkv * min(k, wl.blocks) * 128 * d * elt  # every selected slot valid
+    gather_us = kern[hylra.KERNEL_GATHER][0] * 1e3 if kern[hylra.KERNEL_GATHER][0] else None
+    ceiling = link_ceiling(torch)
+    kv_layer = 2 * B * Hkv * wl.blocks * 128 * d * elt
+    achieved = per_gather / (gather_us * 1e-6) / 1e9 if gather_us else None
+    return {
+        "metric": "offloaded hybrid decode attention steps/s (reuse layers' KV in host memory)",
+        "value": 1000.0 / ms_off, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_off, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V with planted hot blocks; no trained weights)",
+        "config": {"workload": wl.name, "batch": B, "layers": L, "ctx": wl.ctx, "topk": k,
+                   "policy": policy_desc, "offloaded_layers": len(reuse)},
+        "device_hybrid_ms_per_step": ms_dev,
+        "offload_over_device": ms_off / ms_dev,
+        "eager_ms_per_step": ms_eager,
+        "gather": {"avg_launch_us": gather_us, "bytes_per_launch": per_gather,
+                   "achieved_GBps": achieved, "link_peak_GBps": 64.0,
+                   "link_peak_note": "PCIe 5.0 x16, one direction",
+                   "copy_engine_ceiling_GBps": ceiling,
+                   "frac_of_copy_ceiling": achieved / ceiling if achieved else None},
+        "kv_bytes_in_host_memory": kv_layer * len(reuse),
+        "kv_bytes_on_device": kv_layer * (L - len(reuse)),
+        "host_link_bytes_per_step": per_gather * len(reuse),
+        "dense_host_link_bytes_per_step": kv_layer * len(reuse),
     }
 
 
@@ -352,6 +449,10 @@ def main():
         del layers
         torch.cuda.empty_cache()
         print(json.dumps(e2e(args, wl, k, src, policy_desc)), flush=True)
+        return
+    if args.offload:
+        print(json.dumps(offload_bench(args, wl, k, src, policy_desc, layers, torch, hylra)),
+              flush=True)
         return
     n_reset = sum(1 for j, s in enumerate(src) if s == j)
 

@@ -151,6 +151,17 @@ hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, cons
 hylra_status hylra_gather_blocks(const hylra_shape *shape, const hylra_kv *kv, const int32_t *idx,
                                  int32_t k, void *staged_k, void *staged_v, void *hip_stream);
 
+/* Decode-step bookkeeping for a cache that may live in host memory: writes
+ * the new token's k_new and v_new ([B][Hkv][d] device arrays, the pools'
+ * element type) at position pos[b] (device [B]) of each sequence -- K row
+ * [page][g][slot][:] and V column [page][g][slot/32][:][slot%32] with page =
+ * block_table[b][pos/128], slot = pos % 128.  A position outside
+ * [0, 128*max_blocks_per_seq) or a page outside [0, num_pages) writes
+ * nothing.  kv's pools may be device memory or pinned host memory mapped at
+ * the same address (HYLRA_E_INVALID_ARG otherwise); ctx_lens is not read. */
+hylra_status hylra_append_kv(const hylra_shape *shape, const hylra_kv *kv, const void *k_new,
+                             const void *v_new, const int32_t *pos, void *hip_stream);
+
 /* Attention over staged blocks: the result of hylra_decode_sparse on the
  * layer's own pools with the same idx (bit for bit: the same kernel reads the
  * same values in the same order), reading selection slot r of sequence b

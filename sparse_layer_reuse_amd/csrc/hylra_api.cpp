@@ -246,7 +246,7 @@ hylra_status check_gather_source(const hylra_shape *s, const hylra_kv *kv) {
       return st;
     if (!readable)
       return fail(HYLRA_E_INVALID_ARG,
-                  "K/V pools to gather from must be device memory or pinned host memory "
+                  "K/V pools must be device memory or pinned host memory "
                   "(hipHostMalloc) the device maps at the same address, over %zu bytes", bytes);
   }
   return HYLRA_OK;
@@ -414,6 +414,30 @@ hylra_status hylra_gather_blocks(const hylra_shape *shape, const hylra_kv *kv, c
   if (hylra_status st = check_staging(staged_k, staged_v)) return st;
   if (hylra_status st = check_gather_source(shape, kv)) return st;
   if (hylra_status st = run_gather(shape, kv, idx, k, staged_k, staged_v, hip_stream)) return st;
+  return ok();
+}
+
+hylra_status hylra_append_kv(const hylra_shape *shape, const hylra_kv *kv, const void *k_new,
+                             const void *v_new, const int32_t *pos, void *hip_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (hylra_status st = check_kv(kv)) return st;
+  if (k_new == nullptr || v_new == nullptr || pos == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "k_new, v_new and pos must be non-NULL");
+  if (hylra_status st = check_gather_source(shape, kv)) return st;
+  hylra::AppendArgs a{};
+  a.k_pool = const_cast<void *>(kv->k_pool);
+  a.v_pool = const_cast<void *>(kv->v_pool);
+  a.num_pages = kv->num_pages;
+  a.table = kv->block_table;
+  a.pos = pos;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.max_blocks = shape->max_blocks_per_seq;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.elt = (int)elt_bytes(shape);
+  if (hylra_status st = device_status(hylra::launch_append(a, shape->batch, hip_stream), "append launch"))
+    return st;
   return ok();
 }
 

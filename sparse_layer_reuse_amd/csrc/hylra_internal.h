@@ -37,7 +37,7 @@ struct AttnArgs {
   const int32_t *ctx;
   const int32_t *sel;  // nullptr: every block (full); else [B][Hkv][k] block ids
   int staged;          // sparse mode: selection slot r of sequence b sits in page b * k + r
-                       // of a staging pool (table not read)
+                       // of a staging pool (table not read); runs a kernel instance of its own
   int k;
   int max_blocks;
   int num_q_heads;
@@ -82,9 +82,20 @@ struct GatherArgs {
   char *k_dst, *v_dst;
 };
 
+// Append of one decode step's token (hylra_offload.hip): k_new / v_new
+// [B][Hkv][d] written at position pos[b] of each sequence.
+struct AppendArgs {
+  void *k_pool, *v_pool;
+  int64_t num_pages;
+  const int32_t *table, *pos;
+  const void *k_new, *v_new;
+  int max_blocks, num_kv_heads, head_dim, elt;
+};
+
 // Launchers: return 0 on success or the hipError_t code of the launch.
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream);
 int launch_gather(const GatherArgs &a, int batch, void *stream);
+int launch_append(const AppendArgs &a, int batch, void *stream);
 // Cross-stream ordering through a per-device pool of events: event_record
 // records event `slot` on `stream` (after the work enqueued so far),
 // event_wait makes `stream` wait for the last recording of `slot`.

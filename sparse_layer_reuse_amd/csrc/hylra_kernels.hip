@@ -97,6 +97,10 @@ __device__ __forceinline__ int chunk_positions(int T, const int32_t *sel, int k)
 // (all arguments wavefront-uniform).  Returns false when the chunk holds no
 // token to read: past the context, a padding / out-of-range selected id, or a
 // page outside the pool.
+// kStaged: the pools are a staging pool (selection slot r of sequence b in
+// page b * k + r) and no block table is read.  A compile-time choice: a
+// run-time flag in this code slows the regular kernels' selected-block path.
+template <bool kStaged>
 __device__ __forceinline__ bool resolve_chunk(const AttnArgs &a, int b, int g, int T, int pos,
                                               int &page, int &sub, int &valid) {
   int n;
@@ -110,8 +114,10 @@ __device__ __forceinline__ bool resolve_chunk(const AttnArgs &a, int b, int g, i
   valid = T - (n * kBlockTokens + sub * kChunkTokens);
   if (valid <= 0) return false;
   if (valid > kChunkTokens) valid = kChunkTokens;
-  page = a.staged ? b * a.k + pos / kChunksPerBlock
-                  : scalar_load(a.table, (int64_t)b * a.max_blocks + n);
+  if constexpr (kStaged)
+    page = b * a.k + pos / kChunksPerBlock;
+  else
+    page = scalar_load(a.table, (int64_t)b * a.max_blocks + n);
   return page >= 0 && page < a.num_pages;
 }
 
@@ -738,7 +744,7 @@ struct BfTile {
   u32x4 v[D / 16];
 };
 
-template <int D>
+template <int D, bool kStaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_split_bf16(
     AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -784,7 +790,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // and the register tiles never need copying.
   auto issue = [&](BfTile<D> &t, int pos, bool live) -> int {
     int page = 0, sub = 0, valid = 0;
-    const bool ok = live && pos < c_end && resolve_chunk(a, b, g, T, pos, page, sub, valid);
+    const bool ok = live && pos < c_end && resolve_chunk<kStaged>(a, b, g, T, pos, page, sub, valid);
     if (!ok) {
       page = 0;
       sub = 0;
@@ -909,7 +915,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int r = 0; r < 4; ++r) sm.split.o[w][4 * quad + r][16 * n + m16] = acc[n][r];
   __syncthreads();
   if (!finish_split<D>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
-  epilogue<D, D == 128>(a, b, g, T, r.nact, sm.epi);
+  epilogue<D, D == 128 && !kStaged>(a, b, g, T, r.nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -917,7 +923,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // the logits of token t over half of the head dimension for every head of the
 // group; p.V runs with lane i owning columns i and i+64.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool kStaged>
 __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   __shared__ KernelSmem<D> sm;
@@ -955,7 +961,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) cmass[h] = 0.f;
     int page, sub, valid;
-    if (pos < c_end && resolve_chunk(a, b, g, T, pos, page, sub, valid)) {
+    if (pos < c_end && resolve_chunk<kStaged>(a, b, g, T, pos, page, sub, valid)) {
       const int64_t tile = (int64_t)page * Hkv + g;
       const float *krow =
           kpool + (tile * kBlockTokens + sub * kChunkTokens + t) * D + half * (D / 2);
@@ -1136,17 +1142,26 @@ int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *str
   hipStream_t st = static_cast<hipStream_t>(stream);
   const TimerScope tm(a.sel == nullptr ? kTimerFullAttn : kTimerSparseAttn);
   const dim3 block(kThreads);
+#define HYLRA_LAUNCH(K) hipExtLaunchKernelGGL(K, grid, block, 0, st, tm.start, tm.stop, 0, a)
+  const bool staged = a.staged != 0;
   if (dtype == 1) {
-    if (head_dim == 128)
-      hipExtLaunchKernelGGL(attn_split_bf16<128>, grid, block, 0, st, tm.start, tm.stop, 0, a);
-    else
-      hipExtLaunchKernelGGL(attn_split_bf16<64>, grid, block, 0, st, tm.start, tm.stop, 0, a);
+    if (head_dim == 128) {
+      if (staged) HYLRA_LAUNCH((attn_split_bf16<128, true>));
+      else HYLRA_LAUNCH((attn_split_bf16<128, false>));
+    } else {
+      if (staged) HYLRA_LAUNCH((attn_split_bf16<64, true>));
+      else HYLRA_LAUNCH((attn_split_bf16<64, false>));
+    }
   } else {
-    if (head_dim == 128)
-      hipExtLaunchKernelGGL(attn_split_f32<128>, grid, block, 0, st, tm.start, tm.stop, 0, a);
-    else
-      hipExtLaunchKernelGGL(attn_split_f32<64>, grid, block, 0, st, tm.start, tm.stop, 0, a);
+    if (head_dim == 128) {
+      if (staged) HYLRA_LAUNCH((attn_split_f32<128, true>));
+      else HYLRA_LAUNCH((attn_split_f32<128, false>));
+    } else {
+      if (staged) HYLRA_LAUNCH((attn_split_f32<64, true>));
+      else HYLRA_LAUNCH((attn_split_f32<64, false>));
+    }
   }
+#undef HYLRA_LAUNCH
   return (int)hipGetLastError();
 }
 

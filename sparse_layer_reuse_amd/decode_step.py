@@ -13,8 +13,20 @@ attention is this library: a reset
 layer runs hylra_run_policy on that one layer (full attention, fused block
 scores and top-k into the carried index buffer), a reuse layer runs
 hylra_decode_sparse over the carried indices, and the full-attention baseline
-runs hylra_decode_full on every layer.  Weights are random (no trained
-model); the step's shapes are static, so it can be captured as a HIP graph.
+runs hylra_decode_full on every layer.  The new token's K and V go into the
+pages through hylra_append_kv.
+
+Index-guided offloading (technical summary 2.4): offload() moves chosen reuse
+layers' caches to pinned host memory.  In a hybrid step, right after a reset
+layer has selected its blocks, the selected blocks of its offloaded reuse
+layers are gathered to the device on a copy stream (hylra_gather_blocks), so
+the transfers overlap with the projections, MLPs and attention of the layers
+in between; each offloaded layer waits for its own gather and attends over
+the staged blocks (hylra_decode_staged).
+
+Weights are random (no trained model); the step's shapes are static, so it
+can be captured as a HIP graph (the copy stream forks from and joins back
+into the capturing stream).
 """
 from __future__ import annotations
 
@@ -24,10 +36,6 @@ from dataclasses import dataclass
 import torch
 
 from . import hylra, synth
-
-BLOCK = 128
-SUBTILE = 32
-
 
 @dataclass(frozen=True)
 class DecoderShape:
@@ -100,10 +108,23 @@ class RandomDecoder:
                    for l in range(s.layers)]
         t = ctx - 1  # position of the token this step appends
         self.pos = torch.full((batch,), t, dtype=torch.int32, device=device)
-        table = self.kv[0]["table"].long()
-        self.append_page = table[torch.arange(batch, device=device), t // BLOCK]
-        self.append_slot = t % BLOCK
         self.rope_c, self.rope_s = rope_tables(self.pos, s.head_dim, s.rope_theta)
+        self.offloaded = [False] * s.layers
+        self.staging = {}
+        self.copy_stream = None
+        self.gather_done = {}
+
+    def offload(self, layers) -> None:
+        """Moves the caches of `layers` (reuse layers of the policy the steps
+        will run) to pinned host memory."""
+        for l in layers:
+            lay = self.kv[l]
+            lay["k_pool"] = lay["k_pool"].cpu().pin_memory()
+            lay["v_pool"] = lay["v_pool"].cpu().pin_memory()
+            self.offloaded[l] = True
+        if self.copy_stream is None:
+            self.copy_stream = torch.cuda.Stream()
+        torch.cuda.empty_cache()
 
     def dense(self, name: str, l: int) -> torch.Tensor:
         """Layer l's weight `name` (qkv, o, gu, down) as an [in][out] view."""
@@ -113,22 +134,55 @@ class RandomDecoder:
     def append_kv(self, l: int, k: torch.Tensor, v: torch.Tensor) -> None:
         """Writes the step's K and V ([B][Hkv][d]) at position ctx - 1 of every
         sequence: K pages are [page][Hkv][128][d], V pages [page][Hkv][4][d][32]."""
-        slot = self.append_slot
-        kp, vp = self.kv[l]["k_pool"], self.kv[l]["v_pool"]
-        kp[self.append_page, :, slot, :] = k
-        vp[self.append_page, :, slot // SUBTILE, :, slot % SUBTILE] = v
+        lay = self.kv[l]
+        hylra.append_kv(lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
+                        k.contiguous(), v.contiguous(), self.pos)
+
+    def _staging(self, l: int, k: int):
+        key = (l, k)
+        if key not in self.staging:
+            self.staging[key] = hylra.staging_pools(self.kv[l]["k_pool"], self.batch, k)
+        return self.staging[key]
+
+    def _gather_reusers(self, i: int, src, k: int, idx: torch.Tensor) -> None:
+        """After reset layer i: gathers the selected blocks of its offloaded
+        reuse layers on the copy stream, one event per layer."""
+        users = [j for j in range(i + 1, self.shape.layers) if src[j] == i and self.offloaded[j]]
+        if not users:
+            return
+        cs = self.copy_stream
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            for j in users:
+                lay = self.kv[j]
+                sk, sv = self._staging(j, k)
+                hylra.gather_blocks(lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"], idx,
+                                    sk, sv, stream=cs)
+                ev = torch.cuda.Event()
+                ev.record(cs)
+                self.gather_done[j] = ev
 
     def attention(self, l: int, q: torch.Tensor, policy: str, src, k: int, carried):
         lay = self.kv[l]
         if policy == "full":
+            if self.offloaded[l]:
+                raise ValueError("full attention needs every cache on the device")
             out, _, _ = hylra.decode_full(q, lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"])
             return out, carried
         if src[l] == l:
+            if self.offloaded[l]:
+                raise ValueError("layer %d resets and needs its cache on the device" % l)
             idx = torch.empty(1, self.batch, self.shape.num_kv_heads, k, dtype=torch.int32,
                               device=q.device)
             layer = dict(lay, q=q)
             outs, _, _ = hylra.run_policy([layer], [0], k, idx_log=idx)
+            self._gather_reusers(l, src, k, idx[0])
             return outs[0], idx[0]
+        if self.offloaded[l]:
+            torch.cuda.current_stream().wait_event(self.gather_done.pop(l))
+            sk, sv = self._staging(l, k)
+            out, _ = hylra.decode_staged(q, sk, sv, lay["ctx"], carried, lay["table"].shape[1])
+            return out, carried
         out, _ = hylra.decode_sparse(q, lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
                                      carried)
         return out, carried

@@ -63,6 +63,7 @@ def _load():
         "hylra_read_probe": [P, SZ, P, P],
         "hylra_overlap_matrix": [I32, I32, I32, I32, P, P, P],
         "hylra_gather_blocks": [SP, KP, P, I32, P, P, P],
+        "hylra_append_kv": [SP, KP, P, P, P, P],
         "hylra_decode_staged": [SP, P, P, P, P, P, I32, P, P, P, SZ, P],
         "hylra_run_policy_offload": [SP, I32, P, I32, P, KP, P, P, P, P, P, P, P, SZ, P, P],
     }
@@ -82,7 +83,8 @@ _lib = _load()
 EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
             "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_timer_start",
             "hylra_timer_stop", "hylra_overlap_matrix", "hylra_read_probe", "hylra_gather_blocks",
-            "hylra_decode_staged", "hylra_run_policy_offload", "hylra_status_str",
+            "hylra_decode_staged", "hylra_run_policy_offload", "hylra_append_kv",
+            "hylra_status_str",
             "hylra_last_error")
 
 KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_TOPK, KERNEL_GATHER = range(4)
@@ -273,6 +275,22 @@ def gather_blocks(k_pool, v_pool, table, ctx, idx, staged_k, staged_v, *, stream
     shape = Shape(B, Hkv, Hkv, k_pool.shape[3], BLOCK, _DTYPES[k_pool.dtype], table.shape[1], 0.0)
     _check(_lib.hylra_gather_blocks(ctypes.byref(shape), ctypes.byref(kv), _ptr(idx), int(k),
                                     _ptr(staged_k), _ptr(staged_v), _stream(stream)))
+
+
+def append_kv(k_pool, v_pool, table, ctx, k_new, v_new, pos, *, stream=None):
+    """Writes one decode step's k_new / v_new [B][Hkv][d] at positions pos [B]
+    into a layer's pools (on the GPU or pinned in host memory)."""
+    kv = make_kv(k_pool, v_pool, table, ctx, host_ok=True)
+    _need(k_new, "k_new", k_pool.dtype, 3)
+    _need(v_new, "v_new", k_pool.dtype, 3)
+    _need(pos, "pos", torch.int32, 1)
+    B, Hkv, d = k_new.shape
+    if tuple(v_new.shape) != (B, Hkv, d) or pos.shape[0] != B or table.shape[0] != B \
+            or k_pool.shape[1] != Hkv or k_pool.shape[3] != d:
+        raise ValueError("k_new, v_new, pos, block_table and the pools disagree on B, Hkv or d")
+    shape = Shape(B, Hkv, Hkv, d, BLOCK, _DTYPES[k_pool.dtype], table.shape[1], 0.0)
+    _check(_lib.hylra_append_kv(ctypes.byref(shape), ctypes.byref(kv), _ptr(k_new), _ptr(v_new),
+                                _ptr(pos), _stream(stream)))
 
 
 def decode_staged(q, staged_k, staged_v, ctx, idx, max_blocks: int, *, scale=0.0, out=None,

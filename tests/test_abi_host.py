@@ -294,3 +294,14 @@ def test_binding_offload_checks():
     with pytest.raises((ValueError, TypeError)):
         H._check_staging(torch.zeros(3, 2, 128, 64), torch.zeros(3, 2, 4, 64, 32), torch.float32,
                          1, 4, 2, 64)
+
+
+def test_append_argument_checks():
+    lib, s, kv = H._lib, _shape(), _kv()
+    a = lambda kn=FAKE, vn=FAKE, pos=FAKE, kv=kv: lib.hylra_append_kv(
+        ctypes.byref(s), ctypes.byref(kv), kn, vn, pos, None)
+    assert a(kn=None) == H.E_INVALID_ARG
+    assert a(vn=None) == H.E_INVALID_ARG
+    assert a(pos=None) == H.E_INVALID_ARG
+    assert a(kv=_kv(k_pool=None)) == H.E_INVALID_ARG
+    assert a() == H.E_INVALID_ARG  # fake pools the device does not map

@@ -55,13 +55,16 @@ def rel_err(a, b):
     return np.abs(a - b).max() / max(1e-6, np.abs(b).max())
 
 
-@pytest.mark.parametrize("policy", ["hybrid", "full"])
+@pytest.mark.parametrize("policy", ["hybrid", "full", "hybrid-offload"])
 def test_decode_step_layers(D, policy):
     shape = D.DecoderShape(layers=4, hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=64,
                            ffn=512)
     B, ctx, k = 2, 1000, 3
     src = [0, 0, 2, 2]
     dec = D.RandomDecoder(shape, B, ctx, seed=5)
+    if policy == "hybrid-offload":
+        dec.offload([1, 3])  # the reuse layers' caches in pinned host memory
+        policy = "hybrid"
     g = torch.Generator(device="cuda")
     g.manual_seed(9)
     x = torch.randn(B, shape.hidden, generator=g, device="cuda").to(torch.bfloat16)
@@ -77,10 +80,10 @@ def test_decode_step_layers(D, policy):
         assert rel_err(t["v"].float().cpu(), vv) < 2e-2, l
         # the append put the GPU's k / v at position ctx - 1 of the cache
         lay = dec.kv[l]
-        page = lay["table"][:, (ctx - 1) // 128].long()
+        page = lay["table"][:, (ctx - 1) // 128].long().to(lay["k_pool"].device)
         slot = (ctx - 1) % 128
-        assert torch.equal(lay["k_pool"][page, :, slot, :], t["k"])
-        assert torch.equal(lay["v_pool"][page, :, slot // 32, :, slot % 32], t["v"])
+        assert torch.equal(lay["k_pool"][page, :, slot, :].cuda(), t["k"])
+        assert torch.equal(lay["v_pool"][page, :, slot // 32, :, slot % 32].cuda(), t["v"])
         # attention against the oracle on the layer's q and cache
         o = synth.layer_to_oracle(dict(lay, q=t["q"]))
         if policy == "full" or src[l] == l:
@@ -98,3 +101,38 @@ def test_decode_step_layers(D, policy):
         assert np.abs(t["att"].cpu().numpy() - r_out).max() <= 2e-3, l
         # output projection and MLP on the GPU's attention output
         assert rel_err(t["out"].float().cpu(), finish(t["att"])) < 3e-2, l
+
+
+def test_offloaded_step_equals_device_step(D):
+    """The same step with the reuse layers' caches in host memory (gathered
+    on a copy stream) gives the very values of the step with every cache on
+    the device, eager and as a replayed graph."""
+    shape = D.DecoderShape(layers=6, hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                           ffn=512)
+    B, ctx, k = 2, 3000, 4
+    src = [0, 0, 0, 3, 3, 3]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    x = torch.randn(B, shape.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    ref = D.RandomDecoder(shape, B, ctx, seed=8).step(x, "hybrid", src, k)
+    dec = D.RandomDecoder(shape, B, ctx, seed=8)
+    dec.offload([1, 2, 4, 5])
+    out = dec.step(x, "hybrid", src, k)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dec.step(x, "hybrid", src, k)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y = dec.step(x, "hybrid", src, k)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), rep
+        dec.step(x, "hybrid", src, k)  # eager work between replays
+        torch.cuda.synchronize()
