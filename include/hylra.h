@@ -162,6 +162,27 @@ hylra_status hylra_gather_blocks(const hylra_shape *shape, const hylra_kv *kv, c
 hylra_status hylra_append_kv(const hylra_shape *shape, const hylra_kv *kv, const void *k_new,
                              const void *v_new, const int32_t *pos, void *hip_stream);
 
+/* Decode-step helpers around the attention (the end-to-end step puts the
+ * GPU BLAS projections and MLP around this library; these replace chains of
+ * elementwise launches).  bf16 only.
+ *
+ * hylra_rope_append: qkv [B][(Hq + 2 Hkv) d] holds each sequence's new q,
+ * k and v heads in that order.  The q and k heads get the rotary embedding
+ * in the rotate-half form: for i < d/2, (x_i, x_{i+d/2}) becomes
+ * (x_i c - x_{i+d/2} s, x_{i+d/2} c + x_i s) with c = cos_tab[b][i],
+ * s = sin_tab[b][i] (float32 [B][d/2], the cosine and sine of the angle of
+ * position pos[b] for pair i), computed in float32 and rounded to bf16.
+ * Rotated q goes to q_out [B][Hq][d]; rotated k and the v heads are written
+ * at position pos[b] of kv's pages as hylra_append_kv does (same bounds
+ * rule; pools on the device or pinned in host memory).  hylra_silu_mul:
+ * out[r][c] = silu(g) * u with g = gate_up[r][c], u = gate_up[r][width + c]
+ * (gate_up [rows][2 width], out [rows][width], bf16, computed in float32). */
+hylra_status hylra_rope_append(const hylra_shape *shape, const hylra_kv *kv, const void *qkv,
+                               const float *cos_tab, const float *sin_tab, const int32_t *pos,
+                               void *q_out, void *hip_stream);
+hylra_status hylra_silu_mul(const void *gate_up, void *out, int64_t rows, int32_t width,
+                            void *hip_stream);
+
 /* Attention over staged blocks: the result of hylra_decode_sparse on the
  * layer's own pools with the same idx (bit for bit: the same kernel reads the
  * same values in the same order), reading selection slot r of sequence b

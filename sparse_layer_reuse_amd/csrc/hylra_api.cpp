@@ -441,6 +441,47 @@ hylra_status hylra_append_kv(const hylra_shape *shape, const hylra_kv *kv, const
   return ok();
 }
 
+hylra_status hylra_rope_append(const hylra_shape *shape, const hylra_kv *kv, const void *qkv,
+                               const float *cos_tab, const float *sin_tab, const int32_t *pos,
+                               void *q_out, void *hip_stream) {
+  if (hylra_status st = check_shape(shape)) return st;
+  if (shape->dtype != HYLRA_BF16)
+    return fail(HYLRA_E_UNSUPPORTED, "rope_append takes bf16 activations and pools");
+  if (hylra_status st = check_kv(kv)) return st;
+  if (qkv == nullptr || cos_tab == nullptr || sin_tab == nullptr || pos == nullptr || q_out == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "qkv, cos_tab, sin_tab, pos and q_out must be non-NULL");
+  if (hylra_status st = check_gather_source(shape, kv)) return st;
+  hylra::RopeAppendArgs a{};
+  a.qkv = qkv;
+  a.cos_tab = cos_tab;
+  a.sin_tab = sin_tab;
+  a.pos = pos;
+  a.table = kv->block_table;
+  a.q_out = q_out;
+  a.k_pool = const_cast<void *>(kv->k_pool);
+  a.v_pool = const_cast<void *>(kv->v_pool);
+  a.num_pages = kv->num_pages;
+  a.max_blocks = shape->max_blocks_per_seq;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.head_dim = shape->head_dim;
+  if (hylra_status st = device_status(hylra::launch_rope_append(a, shape->batch, hip_stream),
+                                      "rope_append launch"))
+    return st;
+  return ok();
+}
+
+hylra_status hylra_silu_mul(const void *gate_up, void *out, int64_t rows, int32_t width,
+                            void *hip_stream) {
+  if (gate_up == nullptr || out == nullptr)
+    return fail(HYLRA_E_INVALID_ARG, "gate_up and out must be non-NULL");
+  if (rows < 1 || width < 1) return fail(HYLRA_E_INVALID_ARG, "rows and width must be >= 1");
+  if (hylra_status st = device_status(hylra::launch_silu_mul(gate_up, out, rows, width, hip_stream),
+                                      "silu_mul launch"))
+    return st;
+  return ok();
+}
+
 hylra_status hylra_decode_staged(const hylra_shape *shape, const void *q, const void *staged_k,
                                  const void *staged_v, const int32_t *ctx_lens, const int32_t *idx,
                                  int32_t k, float *out, float *lse, void *workspace,

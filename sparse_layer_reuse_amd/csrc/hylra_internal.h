@@ -92,10 +92,24 @@ struct AppendArgs {
   int max_blocks, num_kv_heads, head_dim, elt;
 };
 
+// Rotary embedding of one decode step's q and k fused with the append of k
+// and v (hylra_step.hip); bf16 only.
+struct RopeAppendArgs {
+  const void *qkv;                 // [B][(Hq + 2 Hkv) d]: q heads, k heads, v heads
+  const float *cos_tab, *sin_tab;  // [B][d / 2]
+  const int32_t *pos, *table;
+  void *q_out;                     // [B][Hq][d]
+  void *k_pool, *v_pool;
+  int64_t num_pages;
+  int max_blocks, num_q_heads, num_kv_heads, head_dim;
+};
+
 // Launchers: return 0 on success or the hipError_t code of the launch.
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream);
 int launch_gather(const GatherArgs &a, int batch, void *stream);
 int launch_append(const AppendArgs &a, int batch, void *stream);
+int launch_rope_append(const RopeAppendArgs &a, int batch, void *stream);
+int launch_silu_mul(const void *gu, void *out, int64_t rows, int width, void *stream);
 // Cross-stream ordering through a per-device pool of events: event_record
 // records event `slot` on `stream` (after the work enqueued so far),
 // event_wait makes `stream` wait for the last recording of `slot`.

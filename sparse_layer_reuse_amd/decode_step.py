@@ -7,14 +7,15 @@ projection, rotary position embedding, the append of the new token's K and V
 into the paged cache, attention, the output projection and a SwiGLU MLP.  The
 projections and the MLP are plain library GEMMs (torch on hipBLASLt; each
 weight is stored in the layout whose batch-1..8 GEMV kernel streams fastest,
-and the residual adds ride in the GEMM's beta term) and a few torch
-elementwise ops (fused RMSNorm; RoPE with the step's cos/sin computed once);
+and the residual adds ride in the GEMM's beta term) with torch's fused
+RMSNorm; the rotary embedding of q and k together with the append of k and v
+into the pages is one library launch (hylra_rope_append, with the step's
+cos/sin computed once), and so is the SwiGLU product (hylra_silu_mul);
 attention is this library: a reset
 layer runs hylra_run_policy on that one layer (full attention, fused block
 scores and top-k into the carried index buffer), a reuse layer runs
 hylra_decode_sparse over the carried indices, and the full-attention baseline
-runs hylra_decode_full on every layer.  The new token's K and V go into the
-pages through hylra_append_kv.
+runs hylra_decode_full on every layer.
 
 Index-guided offloading (technical summary 2.4): offload() moves chosen reuse
 layers' caches to pinned host memory.  In a hybrid step, right after a reset
@@ -66,14 +67,12 @@ EPS = 1e-5
 
 
 def rope_tables(pos: torch.Tensor, d: int, theta: float):
-    """cos / signed sin tables [B][1][d] of the rotate-half rotary embedding at
-    positions pos [B]: dimension i < d/2 pairs with i + d/2, both turned by
-    pos * theta^(-2i/d), so x' = x * C + roll(x, d/2) * S."""
+    """cos / sin tables [B][d/2] (float32, from float64 angles) of the
+    rotate-half rotary embedding at positions pos [B]: dimension i < d/2
+    pairs with i + d/2, both turned by the angle pos * theta^(-2i/d)."""
     inv = 1.0 / (theta ** (torch.arange(0, d, 2, device=pos.device, dtype=torch.float64) / d))
-    ang = pos.double()[:, None, None] * inv[None, None, :]
-    cos, sin = torch.cos(ang), torch.sin(ang)
-    return (torch.cat([cos, cos], -1).float().contiguous(),
-            torch.cat([-sin, sin], -1).float().contiguous())
+    ang = pos.double()[:, None] * inv[None, :]
+    return torch.cos(ang).float().contiguous(), torch.sin(ang).float().contiguous()
 
 
 class RandomDecoder:
@@ -108,7 +107,7 @@ class RandomDecoder:
                    for l in range(s.layers)]
         t = ctx - 1  # position of the token this step appends
         self.pos = torch.full((batch,), t, dtype=torch.int32, device=device)
-        self.rope_c, self.rope_s = rope_tables(self.pos, s.head_dim, s.rope_theta)
+        self.rope_c, self.rope_s = rope_tables(self.pos, s.head_dim, s.rope_theta)  # [B][d/2]
         self.offloaded = [False] * s.layers
         self.staging = {}
         self.copy_stream = None
@@ -131,12 +130,16 @@ class RandomDecoder:
         w = getattr(self, "w_" + name)[l]
         return w if name == "gu" else w.t()
 
-    def append_kv(self, l: int, k: torch.Tensor, v: torch.Tensor) -> None:
-        """Writes the step's K and V ([B][Hkv][d]) at position ctx - 1 of every
-        sequence: K pages are [page][Hkv][128][d], V pages [page][Hkv][4][d][32]."""
+    def appended(self, l: int):
+        """The k and v ([B][Hkv][d]) stored at position ctx - 1 of layer l's
+        pages (K pages [page][Hkv][128][d], V pages [page][Hkv][4][d][32])."""
         lay = self.kv[l]
-        hylra.append_kv(lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
-                        k.contiguous(), v.contiguous(), self.pos)
+        t = self.ctx - 1
+        dev = lay["k_pool"].device
+        pages = lay["table"][:, t // 128].long().to(dev)
+        k = lay["k_pool"][pages, :, t % 128, :]
+        v = lay["v_pool"][pages, :, (t % 128) // 32, :, t % 32]
+        return k.cuda(), v.cuda()
 
     def _staging(self, l: int, k: int):
         key = (l, k)
@@ -192,23 +195,23 @@ class RandomDecoder:
         B = x.shape[0]
         x_in = x
         F = torch.nn.functional
-        hq, hkv, d = s.num_q_heads, s.num_kv_heads, s.head_dim
+        lay = self.kv[l]
         h = F.rms_norm(x, (s.hidden,), self.n1[l], EPS)
         qkv = F.linear(h, self.w_qkv[l])
-        # RoPE on the q and k heads together, in float32
-        qk = qkv[:, : (hq + hkv) * d].view(B, hq + hkv, d).float()
-        qk = torch.addcmul(qk * self.rope_c, qk.roll(d // 2, -1), self.rope_s).to(x.dtype)
-        q = qk[:, :hq].contiguous()
-        kk = qk[:, hq:]
-        vv = qkv[:, (hq + hkv) * d:].view(B, hkv, d)
-        self.append_kv(l, kk, vv)
+        q = torch.empty(B, s.num_q_heads, s.head_dim, dtype=x.dtype, device=x.device)
+        hylra.rope_append(qkv, self.rope_c, self.rope_s, self.pos, lay["k_pool"], lay["v_pool"],
+                          lay["table"], lay["ctx"], q, num_q_heads=s.num_q_heads)
         att, carried = self.attention(l, q, policy, src, k, carried)
+        # the first residual out of place (x is the caller's or the trace's),
+        # the second in place
         x = torch.addmm(x, att.view(B, -1).to(x.dtype), self.w_o[l].t())
         gu = F.rms_norm(x, (s.hidden,), self.n2[l], EPS) @ self.w_gu[l]
-        x = torch.addmm(x, F.silu(gu[:, : s.ffn]) * gu[:, s.ffn:], self.w_down[l].t())
+        x.addmm_(hylra.silu_mul(gu), self.w_down[l].t())
         if trace is not None:
+            torch.cuda.synchronize()
+            kk, vv = self.appended(l)
             trace.append({"x": x_in, "q": q, "k": kk, "v": vv, "att": att, "idx": carried,
-                          "out": x})
+                          "out": x.clone()})
         return x, carried
 
     def step(self, x: torch.Tensor, policy: str = "hybrid", src=None, k: int = 16, trace=None):

@@ -64,6 +64,8 @@ def _load():
         "hylra_overlap_matrix": [I32, I32, I32, I32, P, P, P],
         "hylra_gather_blocks": [SP, KP, P, I32, P, P, P],
         "hylra_append_kv": [SP, KP, P, P, P, P],
+        "hylra_rope_append": [SP, KP, P, P, P, P, P, P],
+        "hylra_silu_mul": [P, P, ctypes.c_int64, I32, P],
         "hylra_decode_staged": [SP, P, P, P, P, P, I32, P, P, P, SZ, P],
         "hylra_run_policy_offload": [SP, I32, P, I32, P, KP, P, P, P, P, P, P, P, SZ, P, P],
     }
@@ -84,6 +86,7 @@ EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
             "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_timer_start",
             "hylra_timer_stop", "hylra_overlap_matrix", "hylra_read_probe", "hylra_gather_blocks",
             "hylra_decode_staged", "hylra_run_policy_offload", "hylra_append_kv",
+            "hylra_rope_append", "hylra_silu_mul",
             "hylra_status_str",
             "hylra_last_error")
 
@@ -291,6 +294,41 @@ def append_kv(k_pool, v_pool, table, ctx, k_new, v_new, pos, *, stream=None):
     shape = Shape(B, Hkv, Hkv, d, BLOCK, _DTYPES[k_pool.dtype], table.shape[1], 0.0)
     _check(_lib.hylra_append_kv(ctypes.byref(shape), ctypes.byref(kv), _ptr(k_new), _ptr(v_new),
                                 _ptr(pos), _stream(stream)))
+
+
+def rope_append(qkv, cos_tab, sin_tab, pos, k_pool, v_pool, table, ctx, q_out, *,
+                num_q_heads, stream=None):
+    """Rotary embedding of the new q / k heads in qkv [B][(Hq + 2 Hkv) d]
+    (cos_tab / sin_tab float32 [B][d/2]); rotated q into q_out [B][Hq][d],
+    rotated k and v appended at pos [B] into the layer's pages."""
+    kv = make_kv(k_pool, v_pool, table, ctx, host_ok=True)
+    _need(qkv, "qkv", torch.bfloat16, 2)
+    _need(q_out, "q_out", torch.bfloat16, 3)
+    _need(cos_tab, "cos_tab", torch.float32)
+    _need(sin_tab, "sin_tab", torch.float32)
+    _need(pos, "pos", torch.int32, 1)
+    B = qkv.shape[0]
+    _, Hkv, _, d = k_pool.shape
+    Hq = int(num_q_heads)
+    if k_pool.dtype != torch.bfloat16 or qkv.shape[1] != (Hq + 2 * Hkv) * d \
+            or tuple(q_out.shape) != (B, Hq, d) or pos.shape[0] != B or table.shape[0] != B \
+            or cos_tab.numel() != B * (d // 2) or sin_tab.numel() != B * (d // 2):
+        raise ValueError("rope_append: qkv, q_out, tables, pos and the pools disagree")
+    shape = Shape(B, Hq, Hkv, d, BLOCK, BF16, table.shape[1], 0.0)
+    _check(_lib.hylra_rope_append(ctypes.byref(shape), ctypes.byref(kv), _ptr(qkv), _ptr(cos_tab),
+                                  _ptr(sin_tab), _ptr(pos), _ptr(q_out), _stream(stream)))
+
+
+def silu_mul(gate_up, out=None, *, stream=None):
+    """silu(gate) * up of gate_up [rows][2 width] (bf16) -> [rows][width]."""
+    _need(gate_up, "gate_up", torch.bfloat16, 2)
+    rows, w2 = gate_up.shape
+    out = torch.empty(rows, w2 // 2, dtype=torch.bfloat16, device=gate_up.device) if out is None else out
+    _need(out, "out", torch.bfloat16, 2)
+    if w2 % 2 or tuple(out.shape) != (rows, w2 // 2):
+        raise ValueError("silu_mul: gate_up must be [rows][2 width] and out [rows][width]")
+    _check(_lib.hylra_silu_mul(_ptr(gate_up), _ptr(out), int(rows), int(w2 // 2), _stream(stream)))
+    return out
 
 
 def decode_staged(q, staged_k, staged_v, ctx, idx, max_blocks: int, *, scale=0.0, out=None,

@@ -305,3 +305,18 @@ def test_append_argument_checks():
     assert a(pos=None) == H.E_INVALID_ARG
     assert a(kv=_kv(k_pool=None)) == H.E_INVALID_ARG
     assert a() == H.E_INVALID_ARG  # fake pools the device does not map
+
+
+def test_step_helper_argument_checks():
+    lib, kv = H._lib, _kv()
+    s = _shape()
+    r = lambda shape=s, qkv=FAKE, pos=FAKE, q=FAKE: lib.hylra_rope_append(
+        ctypes.byref(shape), ctypes.byref(kv), qkv, FAKE, FAKE, pos, q, None)
+    assert r(shape=_shape(dtype=H.F32)) == H.E_UNSUPPORTED
+    assert r(qkv=None) == H.E_INVALID_ARG
+    assert r(pos=None) == H.E_INVALID_ARG
+    assert r(q=None) == H.E_INVALID_ARG
+    assert r() == H.E_INVALID_ARG  # fake pools the device does not map
+    assert lib.hylra_silu_mul(None, FAKE, 4, 8, None) == H.E_INVALID_ARG
+    assert lib.hylra_silu_mul(FAKE, FAKE, 0, 8, None) == H.E_INVALID_ARG
+    assert lib.hylra_silu_mul(FAKE, FAKE, 4, 0, None) == H.E_INVALID_ARG

@@ -8,9 +8,12 @@ from sparse_layer_reuse_amd import decode_step as DS
 
 
 def apply_tables(x, pos, theta):
-    c, s = DS.rope_tables(torch.as_tensor(pos), x.shape[-1], theta)
-    xt = torch.from_numpy(x).float()
-    return (xt * c + xt.roll(x.shape[-1] // 2, -1) * s).double().numpy()
+    """The rotation the tables feed (the GPU kernel applies the same per pair)."""
+    d = x.shape[-1]
+    c, s = DS.rope_tables(torch.as_tensor(pos), d, theta)
+    c, s = c.double().numpy()[:, None, :], s.double().numpy()[:, None, :]
+    x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
 def test_rope_tables_match_pairwise_rotation():

