@@ -55,6 +55,8 @@ def parse():
                    help="time a whole random-weight Llama-3-8B-shaped decode step (projections, "
                         "RoPE, KV append, attention, MLP) for the hybrid and the full policy "
                         "instead of attention alone")
+    p.add_argument("--batch", type=int, default=0,
+                   help="override the workload's batch size (sequences per step)")
     p.add_argument("--offload", action="store_true",
                    help="index-guided offloading: the reuse layers' KV caches in pinned host "
                         "memory, their selected blocks gathered on a copy stream (with --e2e: "
@@ -435,6 +437,9 @@ def main():
         import dataclasses
         wl = dataclasses.replace(wl, name="%s_ctx%d" % (wl.name, args.ctx), ctx=args.ctx,
                                  hot_blocks=min(wl.hot_blocks, (args.ctx + 127) // 128))
+    if args.batch:
+        import dataclasses
+        wl = dataclasses.replace(wl, name="%s_b%d" % (wl.name, args.batch), batch=args.batch)
     k = args.topk or wl.topk[0]
     L = min(wl.layers, args.layers or wl.layers)
     t0 = time.time()
