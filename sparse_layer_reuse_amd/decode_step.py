@@ -155,6 +155,7 @@ class RandomDecoder:
             return
         cs = self.copy_stream
         cs.wait_stream(torch.cuda.current_stream())
+        idx.record_stream(cs)  # the allocator keeps idx until the gathers have read it
         with torch.cuda.stream(cs):
             for j in users:
                 lay = self.kv[j]
