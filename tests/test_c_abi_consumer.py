@@ -1,0 +1,86 @@
+"""The C ABI used from plain C (tests/c_abi_consumer.c): no Python binding,
+no torch.  Host-only calls run on the CPU; the GPU case runs a policy step on
+hipMalloc buffers and checks it against the oracle."""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_layer_reuse_amd import build as B
+from sparse_layer_reuse_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+@pytest.fixture(scope="module")
+def consumer(tmp_path_factory):
+    if shutil.which("gcc") is None or not os.path.exists(os.path.join(ROCM, "include", "hip")):
+        pytest.skip("gcc or the HIP headers are missing")
+    if not os.path.exists(B.LIB):
+        pytest.skip("libhylra.so is not built")
+    exe = str(tmp_path_factory.mktemp("c_abi") / "c_abi_consumer")
+    libdir = os.path.dirname(B.LIB)
+    cmd = ["gcc", "-std=c11", "-O1", "-Wall", "-Werror", "-I" + os.path.join(B.ROOT, "include"),
+           "-I" + os.path.join(ROCM, "include"), "-D__HIP_PLATFORM_AMD__",
+           os.path.join(HERE, "c_abi_consumer.c"), "-o", exe, "-L" + libdir, "-lhylra",
+           "-L" + os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + libdir,
+           "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    subprocess.run(cmd, check=True, timeout=120)
+    return exe
+
+
+def test_host_calls_from_c(consumer):
+    res = subprocess.run([consumer, "host"], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stderr
+    assert "host checks ok" in res.stdout
+
+
+@pytest.mark.gpu
+def test_policy_step_from_c(consumer, tmp_path):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("[case] C consumer: policy step on hipMalloc buffers", flush=True)
+    ctx, Hq, Hkv, d, k = (1000, 300), 8, 2, 128, 3
+    src = [0, 0, 2, 2]
+    mb = 8
+    table = synth.block_table(len(ctx), mb, paged=True, seed=5)
+    layers = [synth.make_layer(batch=len(ctx), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                               dtype="bf16", ctx_lens=ctx, seed=90 + 16 * l, table=table,
+                               max_blocks=mb, hot=[[2, 5], [1]], alpha=1.5)
+              for l in range(len(src))]
+    P = layers[0]["k_pool"].shape[0]
+    prob = tmp_path / "problem.bin"
+    with open(prob, "wb") as f:
+        f.write(np.array([len(ctx), Hq, Hkv, d, 1, mb, P, len(src), k], np.int32).tobytes())
+        f.write(np.array(src, np.int32).tobytes())
+        f.write(np.ascontiguousarray(np.asarray(table, np.int32)).tobytes())
+        f.write(np.array(ctx, np.int32).tobytes())
+        for lay in layers:
+            for key in ("q", "k_pool", "v_pool"):
+                f.write(lay[key].contiguous().view(torch.int16).numpy().tobytes())
+    out_path = tmp_path / "result.bin"
+    res = subprocess.run([consumer, "gpu", str(prob), str(out_path)], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    L, Bn = len(src), len(ctx)
+    raw = open(out_path, "rb").read()
+    n_out, n_lse = L * Bn * Hq * d, L * Bn * Hq
+    out = np.frombuffer(raw, np.float32, n_out).reshape(L, Bn, Hq, d)
+    lse = np.frombuffer(raw, np.float32, n_lse, offset=4 * n_out).reshape(L, Bn, Hq)
+    idx = np.frombuffer(raw, np.int32, L * Bn * Hkv * k, offset=4 * (n_out + n_lse))
+    idx = idx.reshape(L, Bn, Hkv, k)
+    ref = oracle.run_policy([synth.layer_to_oracle(l) for l in layers], src, k,
+                            num_kv_heads=Hkv)
+    for j, r in enumerate(ref):
+        if r["margin"] is not None:
+            near = r["margin"] < 1e-5
+            assert np.all(np.all(idx[j] == r["idx"], axis=-1) | near), j
+        else:
+            np.testing.assert_array_equal(idx[j], idx[src[j]])
+        assert np.abs(out[j] - r["out"]).max() <= 2e-3, j
+        assert np.abs(lse[j] - r["lse"]).max() <= 2e-3, j
