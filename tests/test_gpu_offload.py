@@ -102,34 +102,40 @@ def test_gather_and_staged_attention(H, case):
 
 
 def offload_layers(H, ctx, L, seed, dtype="bf16", Hq=32, Hkv=8, d=128):
-    return [gpu_layer(dtype, ctx, Hq, Hkv, d, seed=seed + 16 * l, hot=[[3, 9]] * len(ctx))
+    return [gpu_layer(dtype, ctx, Hq, Hkv, d, seed=seed + 16 * l,
+                      hot=[[3, 9] if T > 9 * 128 else [] for T in ctx])
             for l in range(L)]
 
 
 POLICY_CASES = [
-    # src, offloaded, k
-    ([0, 0, 0, 3, 3, 5], [0, 1, 1, 0, 1, 0], 8),
-    ([0, 0, 2, 2, 2, 2], [0, 1, 0, 1, 1, 1], 3),
-    ([0, 1, 1, 1, 4, 4], [0, 0, 1, 0, 0, 1], 40),  # k past the blocks of the shorter sequence
+    # src, offloaded, k, ctx, (dtype, Hq, Hkv, d)
+    ([0, 0, 0, 3, 3, 5], [0, 1, 1, 0, 1, 0], 8, (5000, 1200), ("bf16", 32, 8, 128)),
+    ([0, 0, 2, 2, 2, 2], [0, 1, 0, 1, 1, 1], 3, (5000, 1200), ("bf16", 32, 8, 128)),
+    # k past the blocks of the shorter sequence
+    ([0, 1, 1, 1, 4, 4], [0, 0, 1, 0, 0, 1], 40, (5000, 1200), ("bf16", 32, 8, 128)),
+    # a sequence with no tokens
+    ([0, 0, 0, 3, 3], [0, 1, 1, 0, 1], 6, (3000, 0, 700), ("bf16", 16, 4, 128)),
+    # float32 K/V, d 64
+    ([0, 0, 2, 2], [0, 1, 0, 1], 4, (2000, 900), ("f32", 8, 2, 64)),
 ]
 
 
-@pytest.mark.parametrize("case", POLICY_CASES, ids=lambda c: "k%d-%s" % (c[2], "".join(map(str, c[1]))))
+@pytest.mark.parametrize("case", POLICY_CASES, ids=lambda c: "k%d-%s-%s-%s" % (
+    c[2], "".join(map(str, c[1])), "_".join(map(str, c[3])), c[4][0]))
 def test_run_policy_offload_matches_oracle(H, case):
-    src, offloaded, k = case
+    src, offloaded, k, ctx, (dtype, Hq, Hkv, d) = case
     say("run_policy_offload", case)
-    ctx = (5000, 1200)
-    layers = offload_layers(H, ctx, len(src), seed=500)
+    layers = offload_layers(H, ctx, len(src), seed=500, dtype=dtype, Hq=Hq, Hkv=Hkv, d=d)
     host_layers = [host_copy(l) if off else l for l, off in zip(layers, offloaded)]
     copy = torch.cuda.Stream()
-    L, B, Hkv = len(src), len(ctx), 8
+    L, B = len(src), len(ctx)
 
     def run(outs, lses):
         idx_log = torch.full((L, B, Hkv, k), -2, dtype=torch.int32, device="cuda")
         plan = H.OffloadPlan(host_layers, src, k, offloaded, outs=outs, lses=lses, idx_log=idx_log)
         return (*plan.run(copy_stream=copy), idx_log)
 
-    checked, outs, lses, idx_log = check_policy_run(H, layers, src, k, "bf16", Hkv, run=run)
+    checked, outs, lses, idx_log = check_policy_run(H, layers, src, k, dtype, Hkv, run=run)
     assert checked == L
     # the same values as the run with every pool on the device
     ref_out, ref_lse, ref_idx = H.run_policy(layers, src, k)
