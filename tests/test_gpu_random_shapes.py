@@ -53,3 +53,37 @@ def test_random_policy_step(H, i):
               for l in range(len(c["src"]))]
     checked, _, _, _ = check_policy_run(H, layers, c["src"], c["k"], c["dtype"], c["Hkv"])
     assert checked == len(c["src"])
+
+
+@pytest.mark.parametrize("i", range(0, N_CASES, 4))
+def test_random_offloaded_step(H, i):
+    """The same shapes with every reuse layer's pools in pinned host memory:
+    the oracle's values, and the very values of the all-device step."""
+    c = random_case(i)
+    say("random shape, offloaded", i, c)
+    src, k = c["src"], c["k"]
+    layers = [gpu_layer(c["dtype"], c["ctx"], c["Hq"], c["Hkv"], c["d"], seed=c["seed"] + 16 * l,
+                        paged=c["paged"], hot=[[1] if T > 256 else [] for T in c["ctx"]])
+              for l in range(len(src))]
+    offloaded = [s != j for j, s in enumerate(src)]
+    host_layers = [dict(l, k_pool=l["k_pool"].cpu().pin_memory(),
+                        v_pool=l["v_pool"].cpu().pin_memory()) if off else l
+                   for l, off in zip(layers, offloaded)]
+    copy = torch.cuda.Stream()
+    L, B = len(src), len(c["ctx"])
+
+    def run(outs, lses):
+        idx_log = torch.full((L, B, c["Hkv"], k), -2, dtype=torch.int32, device="cuda")
+        plan = H.OffloadPlan(host_layers, src, k, offloaded, outs=outs, lses=lses, idx_log=idx_log)
+        return (*plan.run(copy_stream=copy), idx_log)
+
+    checked, outs, lses, idx_log = check_policy_run(H, layers, src, k, c["dtype"], c["Hkv"],
+                                                    run=run)
+    assert checked == L
+    ref_out, ref_lse, ref_idx = H.run_policy(layers, src, k)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_log, ref_idx)
+    for a, b in zip(outs, ref_out):
+        assert torch.equal(a, b)
+    for a, b in zip(lses, ref_lse):
+        assert torch.equal(a, b)
