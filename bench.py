@@ -57,6 +57,9 @@ def parse():
                         "instead of attention alone")
     p.add_argument("--batch", type=int, default=0,
                    help="override the workload's batch size (sequences per step)")
+    p.add_argument("--shard-heads", type=int, default=0, metavar="P",
+                   help="one GPU's share under P-way KV-head (tensor-parallel) sharding: "
+                        "Hkv/P KV heads and Hq/P query heads, the group size unchanged")
     p.add_argument("--offload", action="store_true",
                    help="index-guided offloading: the reuse layers' KV caches in pinned host "
                         "memory, their selected blocks gathered on a copy stream (with --e2e: "
@@ -440,6 +443,16 @@ def main():
     if args.batch:
         import dataclasses
         wl = dataclasses.replace(wl, name="%s_b%d" % (wl.name, args.batch), batch=args.batch)
+    if args.shard_heads:
+        import dataclasses
+        P = args.shard_heads
+        if P < 1 or wl.num_kv_heads % P:
+            print("--shard-heads %d does not divide the %d KV heads" % (P, wl.num_kv_heads),
+                  file=sys.stderr)
+            sys.exit(2)
+        wl = dataclasses.replace(wl, name="%s_tp%d" % (wl.name, P),
+                                 num_kv_heads=wl.num_kv_heads // P,
+                                 num_q_heads=wl.num_q_heads // P)
     k = args.topk or wl.topk[0]
     L = min(wl.layers, args.layers or wl.layers)
     t0 = time.time()
