@@ -30,49 +30,49 @@ __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
 }
 
 constexpr int kStepThreads = 256;
+constexpr int kRopeThreads = 64;  // one wavefront per head vector
 
-// Workgroup b: for every head h of q and k and pair i < d/2, the rotated pair
-// (x_i c - x_{i+d/2} s, x_{i+d/2} c + x_i s); q heads go to q_out, the k
-// heads and the unrotated v heads to the page of position pos[b].
-__global__ __launch_bounds__(kStepThreads) void rope_append(RopeAppendArgs a) {
-  const int b = blockIdx.x;
+// Workgroup (h, b) handles head vector h of sequence b's row of qkv, all of
+// whose elements are independent, so every head runs in parallel: h < Hq is
+// a q head, rotated into q_out; Hq <= h < Hq + Hkv a k head, rotated into the
+// page of position pos[b]; the remaining Hkv heads are v heads, copied as
+// they are into the page's V sub-tile column.  A rotated pair is
+// (x_i c - x_{i+d/2} s, x_{i+d/2} c + x_i s) for i < d/2.
+__global__ __launch_bounds__(kRopeThreads) void rope_append(RopeAppendArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
   const int d = a.head_dim, half = d / 2;
   const int hq = a.num_q_heads, hkv = a.num_kv_heads;
-  const bf16_bits *row = static_cast<const bf16_bits *>(a.qkv) + (int64_t)b * (hq + 2 * hkv) * d;
-  const float *c = a.cos_tab + (int64_t)b * half;
-  const float *s = a.sin_tab + (int64_t)b * half;
-  const int t = a.pos[b];
+  const bf16_bits *row = static_cast<const bf16_bits *>(a.qkv) + ((int64_t)b * (hq + 2 * hkv) + h) * d;
   int page = -1, slot = 0;
-  if (t >= 0 && t < a.max_blocks * kBlockTokens) {
-    const int p = a.table[(int64_t)b * a.max_blocks + t / kBlockTokens];
-    if (p >= 0 && p < a.num_pages) page = p;
-    slot = t % kBlockTokens;
-  }
-  bf16_bits *kp = static_cast<bf16_bits *>(a.k_pool);
-  bf16_bits *vp = static_cast<bf16_bits *>(a.v_pool);
-  bf16_bits *q_out = static_cast<bf16_bits *>(a.q_out) + (int64_t)b * hq * d;
-  // rotated heads: q heads 0..hq-1, then k heads
-  for (int e = threadIdx.x; e < (hq + hkv) * half; e += kStepThreads) {
-    const int h = e / half, i = e % half;
-    const float x0 = bf16_to_f32(row[h * d + i]), x1 = bf16_to_f32(row[h * d + i + half]);
-    const bf16_bits y0 = f32_to_bf16(x0 * c[i] - x1 * s[i]);
-    const bf16_bits y1 = f32_to_bf16(x1 * c[i] + x0 * s[i]);
-    if (h < hq) {
-      q_out[h * d + i] = y0;
-      q_out[h * d + i + half] = y1;
-    } else if (page >= 0) {
-      const int64_t tile = (int64_t)page * hkv + (h - hq);
-      kp[(tile * kBlockTokens + slot) * d + i] = y0;
-      kp[(tile * kBlockTokens + slot) * d + i + half] = y1;
+  if (h >= hq) {  // k and v heads go to the page of position pos[b], if it has one
+    const int t = a.pos[b];
+    if (t >= 0 && t < a.max_blocks * kBlockTokens) {
+      const int p = a.table[(int64_t)b * a.max_blocks + t / kBlockTokens];
+      if (p >= 0 && p < a.num_pages) page = p;
+      slot = t % kBlockTokens;
     }
+    if (page < 0) return;
   }
-  if (page < 0) return;
-  // v heads, as they are: column slot of the page's V sub-tile
-  for (int e = threadIdx.x; e < hkv * d; e += kStepThreads) {
-    const int g = e / d, ch = e % d;
-    const int64_t tile = (int64_t)page * hkv + g;
-    vp[((tile * kChunksPerBlock + slot / kChunkTokens) * d + ch) * kChunkTokens + slot % kChunkTokens] =
-        row[(hq + hkv + g) * d + ch];
+  if (h < hq + hkv) {
+    const float *c = a.cos_tab + (int64_t)b * half;
+    const float *s = a.sin_tab + (int64_t)b * half;
+    bf16_bits *dst;
+    if (h < hq) {
+      dst = static_cast<bf16_bits *>(a.q_out) + ((int64_t)b * hq + h) * d;
+    } else {
+      const int64_t tile = (int64_t)page * hkv + (h - hq);
+      dst = static_cast<bf16_bits *>(a.k_pool) + (tile * kBlockTokens + slot) * d;
+    }
+    for (int i = threadIdx.x; i < half; i += kRopeThreads) {
+      const float x0 = bf16_to_f32(row[i]), x1 = bf16_to_f32(row[i + half]);
+      dst[i] = f32_to_bf16(x0 * c[i] - x1 * s[i]);
+      dst[i + half] = f32_to_bf16(x1 * c[i] + x0 * s[i]);
+    }
+  } else {
+    const int64_t tile = (int64_t)page * hkv + (h - hq - hkv);
+    bf16_bits *vp = static_cast<bf16_bits *>(a.v_pool) +
+                    (tile * kChunksPerBlock + slot / kChunkTokens) * d * kChunkTokens + slot % kChunkTokens;
+    for (int ch = threadIdx.x; ch < d; ch += kRopeThreads) vp[(int64_t)ch * kChunkTokens] = row[ch];
   }
 }
 
@@ -93,7 +93,8 @@ __global__ __launch_bounds__(kStepThreads) void silu_mul(const bf16_bits *gu, bf
 }  // namespace
 
 int launch_rope_append(const RopeAppendArgs &a, int batch, void *stream) {
-  hipLaunchKernelGGL(rope_append, dim3(batch), dim3(kStepThreads), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(rope_append, dim3(a.num_q_heads + 2 * a.num_kv_heads, batch), dim3(kRopeThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 

@@ -203,9 +203,11 @@ class RandomDecoder:
         hylra.rope_append(qkv, self.rope_c, self.rope_s, self.pos, lay["k_pool"], lay["v_pool"],
                           lay["table"], lay["ctx"], q, num_q_heads=s.num_q_heads)
         att, carried = self.attention(l, q, policy, src, k, carried)
-        # the first residual out of place (x is the caller's or the trace's),
-        # the second in place
-        x = torch.addmm(x, att.view(B, -1).to(x.dtype), self.w_o[l].t())
+        # both residuals in place, except where x is the caller's or the trace's
+        if l == 0 or trace is not None:
+            x = torch.addmm(x, att.view(B, -1).to(x.dtype), self.w_o[l].t())
+        else:
+            x.addmm_(att.view(B, -1).to(x.dtype), self.w_o[l].t())
         gu = F.rms_norm(x, (s.hidden,), self.n2[l], EPS) @ self.w_gu[l]
         x.addmm_(hylra.silu_mul(gu), self.w_down[l].t())
         if trace is not None:
