@@ -28,8 +28,9 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def random_log(P, L, S, k, N, seed, empty_frac=0.0):
-    """Random ascending id sets with random valid counts (-1 padding)."""
+def random_log(P, L, S, k, N, seed, empty_frac=0.0, sizes_per_layer=False):
+    """Random ascending id sets with random valid counts (-1 padding): one
+    count per slice, or with sizes_per_layer one per (slice, layer)."""
     rng = np.random.default_rng(seed)
     idx = np.full((P, L, S, k), -1, np.int32)
     for p in range(P):
@@ -38,6 +39,8 @@ def random_log(P, L, S, k, N, seed, empty_frac=0.0):
             if rng.random() < empty_frac:
                 n = 0
             for l in range(L):
+                if sizes_per_layer:
+                    n = int(rng.integers(0, min(k, N) + 1))
                 idx[p, l, s, :n] = np.sort(rng.choice(N, size=n, replace=False))
     return idx
 
@@ -61,6 +64,15 @@ def test_overlap_golden(H):
 def test_overlap_random(H, P, L, S, k, N):
     say("overlap", P, L, S, k, N)
     check(H, random_log(P, L, S, k, N, seed=P * 1000 + L * 10 + k, empty_frac=0.2))
+
+
+@pytest.mark.parametrize("P,L,S,k,N", [(1, 6, 4, 8, 12), (2, 20, 3, 40, 100)],
+                         ids=lambda v: str(v))
+def test_overlap_random_sizes_per_layer(H, P, L, S, k, N):
+    # source and target sets of one slice differ in size: the ratio is over
+    # the target's set
+    say("overlap sizes per layer", P, L, S, k, N)
+    check(H, random_log(P, L, S, k, N, seed=7 + L, sizes_per_layer=True))
 
 
 def test_overlap_from_all_reset_run(H):

@@ -49,6 +49,17 @@ def test_overlap_padding_and_empty_slices():
     np.testing.assert_array_equal(oracle.overlap_matrix(none), np.zeros((3, 3), np.float32))
 
 
+def test_overlap_ratio_is_over_the_target_set():
+    # reading of the overlap ratio: shared ids over the target layer's set.
+    # Layer 0 selects {3, 8}, layer 1 {1, 3, 5, 8}, layer 2 {3, 8} (-1 padded);
+    # over the source's set instead, M[1][0] would be 1 and M[2][1] 1/2.
+    idx = np.array([[[[3, 8, -1, -1]], [[1, 3, 5, 8]], [[3, 8, -1, -1]]]], np.int32)
+    M = oracle.overlap_matrix(idx)
+    assert M[1, 0] == np.float32(2 / 4)
+    assert M[2, 1] == np.float32(2 / 2)
+    assert M[2, 0] == np.float32(1.0)
+
+
 def test_overlap_identical_and_disjoint_layers():
     rng = np.random.default_rng(3)
     base = np.sort(rng.choice(100, size=(2, 1, 5, 10), replace=False, axis=-1), axis=-1)

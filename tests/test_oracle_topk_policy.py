@@ -89,12 +89,22 @@ def test_run_policy_k_covering_all_blocks_equals_full():
 def test_run_policy_reuse_uses_source_indices():
     layers = _tiny_layers(ctx=(1024,))
     res = oracle.run_policy(layers, [0, 0, 2, 2], 2, num_kv_heads=2)
+    # each reset layer carries its own top-k (the two differ here, so a reuse
+    # layer that kept an older reset's set would be seen)
+    for j in (0, 2):
+        lay = layers[j]
+        _, _, score = oracle.decode_full(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"],
+                                         lay["ctx"], num_kv_heads=2)
+        np.testing.assert_array_equal(res[j]["idx"], oracle.topk(score, lay["ctx"], 2)[0])
+    assert not np.array_equal(res[0]["idx"], res[2]["idx"])
     assert np.array_equal(res[1]["idx"], res[0]["idx"])
     assert np.array_equal(res[3]["idx"], res[2]["idx"])
-    lay = layers[1]
-    out, lse, _ = oracle.attend(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
-                                num_kv_heads=2, sel=res[0]["idx"], k=2)
-    np.testing.assert_array_equal(res[1]["out"], out)
+    for j, source in ((1, 0), (3, 2)):
+        lay = layers[j]
+        out, lse, _ = oracle.attend(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"],
+                                    lay["ctx"], num_kv_heads=2, sel=res[source]["idx"], k=2)
+        np.testing.assert_array_equal(res[j]["out"], out)
+        np.testing.assert_array_equal(res[j]["lse"], lse)
 
 
 def test_run_policy_rejects_malformed():
