@@ -89,8 +89,23 @@ struct Workspace {
   float *stats;
   int32_t *counters;
   int32_t *idx;
+  float *part_ml2;  // two-level merge of the full plan only, else null
+  float *part_o2;
   size_t bytes;
 };
+
+// Whether a full-mode launch of this shape merges its split partials in two
+// levels: one merging workgroup per (sequence, KV head) would read more than
+// kOneLevelMergeBytes of partials (~90 GB/s through one compute unit).  Only
+// the bf16, d = 128 kernel has the two-level instance; its group counters
+// must fit the upper half of the counter region.
+bool two_level_merge(const hylra_shape *s, const hylra::SplitPlan &p) {
+  const long part_bytes = (long)(s->num_q_heads / s->num_kv_heads) * s->head_dim * 4;
+  return s->dtype == HYLRA_BF16 && s->head_dim == 128 &&
+         (long)p.nsplit * part_bytes > hylra::kOneLevelMergeBytes &&
+         (long)s->batch * s->num_kv_heads * hylra::kMaxGroups <=
+             hylra::kCounterSlots - hylra::kGroupCounterBase;
+}
 
 int max_nsplit(const hylra_shape *s, int k) {
   const hylra::SplitPlan f = hylra::plan_full(s->batch, s->num_kv_heads, s->max_blocks_per_seq);
@@ -124,6 +139,10 @@ Workspace layout(const hylra_shape *s, int k, void *base) {
   w.part_o = reinterpret_cast<float *>(take(B * Hq * ns * D * sizeof(float)));
   w.stats = reinterpret_cast<float *>(take(B * Hq * mb * sizeof(float)));
   w.idx = reinterpret_cast<int32_t *>(take(B * Hkv * (size_t)(k > 0 ? k : 1) * sizeof(int32_t)));
+  if (two_level_merge(s, hylra::plan_full(s->batch, s->num_kv_heads, s->max_blocks_per_seq))) {
+    w.part_ml2 = reinterpret_cast<float *>(take(B * Hq * hylra::kMaxGroups * 2 * sizeof(float)));
+    w.part_o2 = reinterpret_cast<float *>(take(B * Hq * hylra::kMaxGroups * D * sizeof(float)));
+  }
   w.bytes = off;
   return w;
 }
@@ -164,6 +183,8 @@ hylra::AttnArgs attn_args(const hylra_shape *s, const void *q, const hylra_kv *k
   a.part_ml = w.part_ml;
   a.part_o = w.part_o;
   a.counters = w.counters;
+  a.part_ml2 = w.part_ml2;
+  a.part_o2 = w.part_o2;
   return a;
 }
 
@@ -175,6 +196,7 @@ hylra_status run_full(const hylra_shape *s, const void *q, const hylra_kv *kv, f
   const hylra::SplitPlan plan = hylra::plan_full(s->batch, s->num_kv_heads, s->max_blocks_per_seq);
   hylra::AttnArgs a = attn_args(s, q, kv, nullptr, k, plan, w);
   a.stats = (block_score != nullptr || idx != nullptr) ? w.stats : nullptr;
+  a.two_level = two_level_merge(s, plan) ? 1 : 0;
   a.out = out;
   a.lse = lse;
   a.score_out = block_score;

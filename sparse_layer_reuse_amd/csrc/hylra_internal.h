@@ -15,6 +15,15 @@ constexpr int kMaxSplits = 256;    // workgroups per (sequence, KV head)
 constexpr int kCounterSlots = 65536;  // (sequence, KV head) arrival counters in a workspace
 constexpr int kMaxWgChunks = 256;     // chunk positions per workgroup (64 blocks)
 constexpr int kWavesPerGroup = 8;     // wavefronts per workgroup (one workgroup per CU)
+// Two-level merge (full mode, many splits): the last arrival of each group of
+// kGroupSplits consecutive splits merges the group into one partial, and the
+// last group to finish merges the group partials.  Group arrival counters
+// sit in the upper half of the counter region.
+constexpr int kGroupSplits = 16;
+constexpr int kMaxGroups = kMaxSplits / kGroupSplits;
+constexpr int kGroupCounterBase = kCounterSlots / 2;
+constexpr long kOneLevelMergeBytes = 512l << 10;  // above this many partial bytes per
+                                                  // (sequence, KV head): two levels
 
 // Work split of one attention launch: each workgroup (8 wavefronts) takes
 // `chunks_per_wg` consecutive 32-token chunk positions of one (sequence, KV
@@ -51,6 +60,9 @@ struct AttnArgs {
   float *part_o;       // [B][Hq][nsplit][d]  unnormalised output
   float *stats;        // full mode with scores: [B][Hq][max_blocks] block mass, relative to
                        // the running max of the block's workgroup partial
+  int two_level;       // split partials merged in groups first (bf16, d = 128 only)
+  float *part_ml2;     // two-level: [B][Hq][kMaxGroups][2]  group max (log2 units) and sum
+  float *part_o2;      // two-level: [B][Hq][kMaxGroups][d]  group output, relative to its max
   int32_t *counters;   // [B][Hkv] arrival counters, zero between launches
   // outputs
   float *out;          // [B][Hq][d]

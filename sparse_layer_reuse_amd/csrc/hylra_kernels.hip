@@ -228,6 +228,7 @@ struct SplitSmem {
 // LDS used by the epilogue and the top-k selection.
 struct EpiSmem {
   float f[kMaxGroup][kMaxSplits];  // per (head, split) rescale factor 2^(m_s - M)
+  float f2[kMaxGroup][kMaxGroups]; // two-level: per (head, group) factor 2^(m_q - M)
   float M[kMaxGroup];
   float L[kMaxGroup];
   float invL[kMaxGroup];
@@ -401,11 +402,58 @@ __device__ __forceinline__ void write_empty(const AttnArgs &a, int b, int g, int
     }
 }
 
+// Two-level merge, run by the last workgroup of group q to arrive: the
+// partials of its gsize splits q*kGroupSplits ... become one group partial
+// (max m_q over the splits, sum and output rescaled to m_q), stored with
+// coherent stores like the split partials.  Thread (h, c) handles 4 columns
+// of one head; every load is issued before the first use.
+template <int D>
+__device__ __forceinline__ void merge_group(const AttnArgs &a, int b, int g, int q, int gsize) {
+  const int G = a.group;
+  if ((int)threadIdx.x >= G * (D / 4)) return;
+  const int h = threadIdx.x / (D / 4), c = 4 * (threadIdx.x % (D / 4));
+  const int64_t row = ((int64_t)b * a.num_q_heads + g * G + h);
+  const int s0 = q * kGroupSplits;
+  const __amdgpu_buffer_rsrc_t pml = buffer(a.part_ml + (row * a.nsplit + s0) * 2, (uint32_t)(gsize * 2 * 4));
+  const __amdgpu_buffer_rsrc_t po = buffer(a.part_o + (row * a.nsplit + s0) * D, (uint32_t)(gsize * D * 4));
+  float m[kGroupSplits], l[kGroupSplits];
+  f32x4 o[kGroupSplits];
+#pragma unroll
+  for (int j = 0; j < kGroupSplits; ++j) {
+    const uint32_t ml_off = j < gsize ? (uint32_t)(j * 2 * 4) : 0x80000000u;
+    const uint32_t o_off = j < gsize ? (uint32_t)((j * D + c) * 4) : 0x80000000u;
+    m[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pml, ml_off, 0, kCoherent));
+    l[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pml, ml_off + 4u, 0, kCoherent));
+    o[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(po, o_off, 0, kCoherent));
+  }
+  float mq = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kGroupSplits; ++j)
+    if (j < gsize) mq = fmaxf(mq, m[j]);
+  float lq = 0.f;
+  f32x4 oq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kGroupSplits; ++j) {
+    const float f = j < gsize ? rescale(m[j], mq) : 0.f;
+    lq += f * l[j];
+    oq += f * o[j];
+  }
+  const __amdgpu_buffer_rsrc_t po2 = buffer(a.part_o2 + row * kMaxGroups * D, (uint32_t)(kMaxGroups * D * 4));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oq), po2, (uint32_t)((q * D + c) * 4), 0,
+                                         kCoherent);
+  if (c == 0) {
+    store_agent(a.part_ml2 + (row * kMaxGroups + q) * 2 + 0, mq);
+    store_agent(a.part_ml2 + (row * kMaxGroups + q) * 2 + 1, lq);
+  }
+}
+
 // Writes the workgroup partial from the eight wavefront states (and, in full
 // mode with scores, the block masses rescaled to the partial's max), then
 // counts the workgroup's arrival.  Returns true in the last of the nact
-// workgroups of (b, g), which then runs the epilogue.
-template <int D>
+// workgroups of (b, g), which then runs the epilogue.  Two-level: the
+// arrival is first counted in the split's group; the group's last arrival
+// merges the group and counts it among the groups of (b, g).
+template <int D, bool kTwoLevel = false>
 __device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact, int c_begin,
                              int c_end, int T, SplitSmem<D> &sm, int *last_flag) {
   const int G = a.group;
@@ -457,10 +505,29 @@ __device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, in
   // the last arrival then reads everyone's.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (kTwoLevel) {
+    const int q = s / kGroupSplits;
+    const int gsize = min(kGroupSplits, nact - q * kGroupSplits);
+    if (threadIdx.x == 0) {
+      int32_t *cnt = a.counters + kGroupCounterBase + ((int64_t)b * a.num_kv_heads + g) * kMaxGroups + q;
+      const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = prev == gsize - 1;
+      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *last_flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    const bool group_last = *last_flag != 0;
+    __syncthreads();
+    if (!group_last) return false;
+    merge_group<D>(a, b, g, q, gsize);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
     int32_t *cnt = a.counters + (int64_t)b * a.num_kv_heads + g;
+    const int arrivals = kTwoLevel ? (nact + kGroupSplits - 1) / kGroupSplits : nact;
     const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == nact - 1;
+    const bool last = prev == arrivals - 1;
     if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *last_flag = last ? 1 : 0;
   }
@@ -484,7 +551,7 @@ __device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, in
 // larger shapes (a second head per wavefront, more than 64 splits, blocks
 // past kThreads) sit behind branches.  A lane out of range reads at an
 // offset past the resource, which gives 0 without touching memory.
-template <int D, int kBatch, int GP>
+template <int D, int kBatch, int GP, bool kTwoLevel = false>
 __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
   const int G = a.group;
   const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
@@ -494,15 +561,20 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
   const int item = threadIdx.x % items, stripe = threadIdx.x / items;
   const bool active = stripe < stripes;
   const int h_item = item / (D / 4), c_item = 4 * (item % (D / 4));
-  const __amdgpu_buffer_rsrc_t po = buffer(a.part_o + head0 * a.nsplit * D,
-                                           (uint32_t)(G * a.nsplit * D * 4));
-  // loads of splits stripe + stripes * (j0 + j)
+  // the partials the output merge reads: the splits', or with two levels the
+  // groups'
+  const int nparts = kTwoLevel ? (nact + kGroupSplits - 1) / kGroupSplits : nact;
+  const int pstride = kTwoLevel ? kMaxGroups : a.nsplit;
+  const __amdgpu_buffer_rsrc_t po =
+      kTwoLevel ? buffer(a.part_o2 + head0 * kMaxGroups * D, (uint32_t)(G * kMaxGroups * D * 4))
+                : buffer(a.part_o + head0 * a.nsplit * D, (uint32_t)(G * a.nsplit * D * 4));
+  // loads of partials stripe + stripes * (j0 + j)
   auto load_batch = [&](f32x4 (&v)[kBatch], int j0) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int s = stripe + stripes * (j0 + j);
-      const uint32_t off = (active && s < nact)
-                               ? (uint32_t)(((h_item * a.nsplit + s) * D + c_item) * 4)
+      const uint32_t off = (active && s < nparts)
+                               ? (uint32_t)(((h_item * pstride + s) * D + c_item) * 4)
                                : 0x80000000u;
       v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(po, off, 0, kCoherent));
     }
@@ -527,6 +599,20 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
   load_ml(0, 0, ms[0][0], ls[0][0]);
   f32x4 first[kBatch];
   load_batch(first, 0);
+  // two levels: the group maxima of heads w and w + kWaves (lane q: group q)
+  float m2[HH];
+  if constexpr (kTwoLevel) {
+    const __amdgpu_buffer_rsrc_t pml2 =
+        buffer(a.part_ml2 + head0 * kMaxGroups * 2, (uint32_t)(G * kMaxGroups * 2 * 4));
+#pragma unroll
+    for (int hh = 0; hh < HH; ++hh) {
+      const int h = w + kWaves * hh;
+      const bool in = h < G && lane < nparts;
+      const uint32_t off = in ? (uint32_t)((h * kMaxGroups + lane) * 2 * 4) : 0x80000000u;
+      const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(pml2, off, 0, kCoherent);
+      m2[hh] = in ? __builtin_bit_cast(float, bits) : kNegInf;
+    }
+  }
   // block masses (stored relative to their split's max) of block threadIdx.x
   const __amdgpu_buffer_rsrc_t pst =
       buffer(a.stats != nullptr ? a.stats + head0 * a.max_blocks : nullptr,
@@ -583,6 +669,9 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
       if (s < nact) sm.f[h][s] = f;
       lsum += f * ls[hh][j];
     }
+    if constexpr (kTwoLevel) {
+      if (lane < nparts) sm.f2[h][lane] = rescale(m2[hh], M);
+    }
     const float L = wave_sum(lsum);
     if (lane == 0) {
       sm.M[h] = M;
@@ -594,12 +683,18 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
 
   f32x4 out_v = {0.f, 0.f, 0.f, 0.f};
   {
-    const int per_stripe = (nact - stripe + stripes - 1) / stripes;  // splits of this stripe
+    const int per_stripe = (nparts - stripe + stripes - 1) / stripes;  // partials of this stripe
+    auto factor = [&](int s) {
+      if constexpr (kTwoLevel)
+        return sm.f2[h_item][s];
+      else
+        return sm.f[h_item][s];
+    };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int s = stripe + stripes * j;
-      if (active && s < nact) acc += sm.f[h_item][s] * first[j];
+      if (active && s < nparts) acc += factor(s) * first[j];
     }
     for (int j0 = kBatch; j0 < per_stripe; j0 += kBatch) {
       f32x4 v[kBatch];
@@ -607,7 +702,7 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int s = stripe + stripes * (j0 + j);
-        if (active && s < nact) acc += sm.f[h_item][s] * v[j];
+        if (active && s < nparts) acc += factor(s) * v[j];
       }
     }
     if (stripes > 1) {
@@ -685,9 +780,11 @@ __device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, i
 // and register allocation shrink, and the extra filler loads of a loose fit
 // cost less.  Only the bf16 kernel with d = 128 (the large shapes) gets the
 // specialised instances; the others use one generic instance.
-template <int D, bool kSpecialise>
+template <int D, bool kSpecialise, bool kTwoLevel = false>
 __device__ __forceinline__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
-  if constexpr (!kSpecialise) {
+  if constexpr (kTwoLevel) {
+    epilogue_impl<D, 8, kMaxGroup, true>(a, b, g, T, nact, sm);
+  } else if constexpr (!kSpecialise) {
     epilogue_impl<D, 8, kMaxGroup>(a, b, g, T, nact, sm);
   } else {
     const int G = uniform(a.group);
@@ -745,7 +842,7 @@ struct BfTile {
   u32x4 v[D / 16];
 };
 
-template <int D, bool kStaged>
+template <int D, bool kStaged, bool kTwoLevel = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_split_bf16(
     AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -915,8 +1012,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.split.o[w][4 * quad + r][16 * n + m16] = acc[n][r];
   __syncthreads();
-  if (!finish_split<D>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
-  epilogue<D, D == 128 && !kStaged>(a, b, g, T, r.nact, sm.epi);
+  if (!finish_split<D, kTwoLevel>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
+  epilogue<D, D == 128 && !kStaged, kTwoLevel>(a, b, g, T, r.nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1148,6 +1245,7 @@ int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *str
   if (dtype == 1) {
     if (head_dim == 128) {
       if (staged) HYLRA_LAUNCH((attn_split_bf16<128, true>));
+      else if (a.two_level) HYLRA_LAUNCH((attn_split_bf16<128, false, true>));
       else HYLRA_LAUNCH((attn_split_bf16<128, false>));
     } else {
       if (staged) HYLRA_LAUNCH((attn_split_bf16<64, true>));

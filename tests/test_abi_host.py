@@ -138,6 +138,31 @@ def test_workspace_size_grows_with_k_and_context():
         assert H.workspace_size(sh, max(wl.topk)) < 0.05 * wl.kv_bytes_per_layer() + 262144 + 4096
 
 
+def test_workspace_adds_group_partials_only_for_two_level_merges():
+    # A full-mode launch merges in two levels when one (sequence, KV head)
+    # has more than 512 KiB of split partials (bf16, d = 128): then the
+    # workspace also holds [B][Hq][16] group partials of d + 2 floats.
+    def size(B, Hq, Hkv, mb, dtype=H.BF16, d=128):
+        return H.workspace_size(H.Shape(B, Hq, Hkv, d, 128, dtype, mb, 0.0), 0)
+
+    def extra(B, Hq, d=128):
+        return B * Hq * 16 * (d + 2) * 4
+
+    # 256 splits x 8 heads x 128 x 4 B = 1 MiB per (sequence, KV head): two levels
+    one_head = size(1, 8, 1, 1024)
+    # the same context over 8 KV heads: 32 splits, 128 KiB: one level
+    eight_heads = size(1, 64, 8, 1024)
+    base = lambda B, Hq, Hkv, mb, ns, d=128: (65536 * 4 + B * Hq * ns * (d + 2) * 4
+                                               + B * Hq * mb * 4 + B * Hkv * 4)
+    assert one_head >= base(1, 8, 1, 1024, 256) + extra(1, 8)
+    assert eight_heads < base(1, 64, 8, 1024, 32) + 4096
+    # exactly 512 KiB (4-way shard of the 70B shape: 128 splits x 4 KiB): one level
+    assert size(2, 8, 1, 1024) < base(2, 8, 1, 1024, 128) + 4096
+    # the float32 kernel and d = 64 keep one level
+    assert size(1, 8, 1, 1024, dtype=H.F32) < base(1, 8, 1, 1024, 256) + 4096
+    assert size(1, 16, 1, 1024, d=64) < base(1, 16, 1, 1024, 256, d=64) + 4096
+
+
 def test_policy_dp_argument_checks():
     M = np.zeros((3, 3), np.float32)
     with pytest.raises(H.HylraError):

@@ -500,6 +500,45 @@ def test_merge_generic_instance_d64_many_splits(H):
     assert np.all(np.all(got == want, axis=-1) | (margin < MARGIN))
 
 
+# Full mode merges in two levels when one (sequence, KV head) has more than
+# 512 KiB of split partials (splits * G * d * 4 bytes): each group of 16
+# splits is merged by its last arrival, then the last group merges the
+# groups.  One KV head and long contexts give up to 256 splits.
+TWO_LEVEL_CASES = [
+    # (group, contexts)
+    (8, (131072,)),          # 256 splits of 4 KiB: 16 full groups
+    (5, (120000,)),          # 235 splits of 2.5 KiB: a last group of 11, a partial last block
+    (16, (32768,)),          # 128 splits of 8 KiB
+    (12, (65536, 30000)),    # 128 splits of 6 KiB; the second sequence has 59 (a last group of 11)
+    (12, (65536, 0)),        # an empty sequence beside a two-level one
+]
+
+
+@pytest.mark.parametrize("G,ctx", TWO_LEVEL_CASES, ids=lambda v: str(v))
+def test_two_level_merge_reset_and_reuse(H, G, ctx):
+    say("two-level merge G", G, "ctx", ctx)
+    hot = [[1, (max(c, 1) - 1) // 128] for c in ctx]
+    layers = [gpu_layer("bf16", ctx, G, 1, 128, seed=3100 + 31 * G + 16 * l, hot=hot, alpha=2.0)
+              for l in range(2)]
+    n, *_ = check_policy_run(H, layers, [0, 0], 8, "bf16", 1)
+    assert n == 2
+
+
+def test_two_level_merge_without_scores(H):
+    ctx = (131072, 90000)
+    say("two-level merge, no scores", ctx)
+    lay = gpu_layer("bf16", ctx, 12, 1, 128, seed=3333)
+    o0, l0 = nan_out(lay["q"])
+    out, lse, _ = H.decode_full(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
+                                out=o0, lse=l0)
+    assert counters_are_zero(H, lay["q"], lay["k_pool"], lay["table"])
+    o = synth.layer_to_oracle(lay)
+    r_out, r_lse, _ = oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
+                                    num_kv_heads=1)
+    assert_close(out.cpu().numpy(), r_out, TOL["bf16"], "out")
+    assert_close(lse.cpu().numpy(), r_lse, TOL["bf16"], "lse")
+
+
 def test_max_context_fused_topk_and_reuse(H):
     """The largest context the ABI takes: 8192 blocks (1M tokens) for one
     sequence and KV head with 16 query heads; the reset layer's fused scores
