@@ -537,7 +537,7 @@ def main():
         "kernel_launches": {hylra.KERNEL_NAMES[kk]: kern[kk][1] for kk in ALL},
         "sparse_attn_gbs": (sparse_bytes / (sparse_us * 1e-6) / 1e9) if sparse_us else None,
         "roofline": {
-            "kernel": ("attn_split_bf16<%d, false>" if wl.dtype == "bf16" else "attn_split_f32<%d, false>")
+            "kernel": ("attn_split_bf16<%d, false, false>" if wl.dtype == "bf16" else "attn_split_f32<%d, false>")
                       % d + " full mode (reset layer: split pass + fused merge/score/top-k)",
             "bound": "hbm",
             "achieved": achieved,
