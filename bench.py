@@ -388,7 +388,8 @@ def offload_bench(args, wl, k, src, policy_desc, layers, torch, hylra):
     copy = torch.cuda.Stream()
     plan = hylra.OffloadPlan(host_layers, src, k, offloaded)
     # eager steps with the gather and attention kernels timed
-    kinds = (hylra.KERNEL_GATHER, hylra.KERNEL_SPARSE_ATTN, hylra.KERNEL_FULL_ATTN)
+    kinds = (hylra.KERNEL_GATHER, hylra.KERNEL_SPARSE_ATTN, hylra.KERNEL_FULL_ATTN,
+             hylra.KERNEL_FULL_SCORED)
     ms_eager, kern = timed(lambda: plan.run(copy_stream=copy), args.steps, args.warmup, torch,
                            kinds, hylra)
     ms_off, g = graph_timed(lambda: plan.run(copy_stream=copy), args.steps, args.warmup, torch)
@@ -475,7 +476,7 @@ def main():
     n_reset = sum(1 for j, s in enumerate(src) if s == j)
 
     hybrid = hylra.PolicyPlan(layers, src, k)
-    ALL = (hylra.KERNEL_FULL_ATTN, hylra.KERNEL_SPARSE_ATTN)
+    ALL = (hylra.KERNEL_FULL_SCORED, hylra.KERNEL_FULL_ATTN, hylra.KERNEL_SPARSE_ATTN)
     # eager steps with per-kernel HIP events (per-layer latency, roofline)
     ms_eager, kern = timed(hybrid.run, args.steps, args.warmup, torch, ALL, hylra)
     # the step as one HIP graph (how a decode loop replays a static step): value
@@ -508,7 +509,14 @@ def main():
     full_bytes = 2 * B * Hkv * T * d * elt          # K and V of every token, once
     sparse_bytes = 2 * B * Hkv * min(k, wl.blocks) * 128 * d * elt
     us = lambda kind: (kern[kind][0] * 1e3) if kern[kind][0] is not None else None
-    full_us, sparse_us = us(hylra.KERNEL_FULL_ATTN), us(hylra.KERNEL_SPARSE_ATTN)
+    scored_us, plain_us = us(hylra.KERNEL_FULL_SCORED), us(hylra.KERNEL_FULL_ATTN)
+    sparse_us = us(hylra.KERNEL_SPARSE_ATTN)
+    # the roofline kernel: the reset layer whose index set is used (full
+    # attention + fused block scores + top-k); a policy without one falls back
+    # to the plain full-attention launch
+    full_us = scored_us if scored_us is not None else plain_us
+    roof_kind = "full mode with fused block scores and top-k" if scored_us is not None \
+        else "full mode without block scores"
     achieved = full_bytes / (full_us * 1e-6) / 1e9
     out = {
         "metric": METRIC,
@@ -529,7 +537,8 @@ def main():
             "paged": wl.paged, "policy": policy_desc, "resets": n_reset, "reuses": L - n_reset,
         },
         "per_layer_us": {
-            "reset_layer": full_us,
+            "reset_layer_with_topk": scored_us,
+            "reset_layer_without_topk": plain_us,
             "reuse_layer": sparse_us,
             "wall_avg": ms_h * 1e3 / L,
         },
@@ -537,8 +546,8 @@ def main():
         "kernel_launches": {hylra.KERNEL_NAMES[kk]: kern[kk][1] for kk in ALL},
         "sparse_attn_gbs": (sparse_bytes / (sparse_us * 1e-6) / 1e9) if sparse_us else None,
         "roofline": {
-            "kernel": ("attn_split_bf16<%d, false, false>" if wl.dtype == "bf16" else "attn_split_f32<%d, false>")
-                      % d + " full mode (reset layer: split pass + fused merge/score/top-k)",
+            "kernel": ("attn_split_bf16 (d=%d)" if wl.dtype == "bf16" else "attn_split_f32 (d=%d)")
+                      % d + ", " + roof_kind,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -29,7 +29,13 @@
  *       ctx_lens     [B] int32, tokens of each sequence (device memory)
  *       out          [B][Hq][d] float32, lse [B][Hq] float32 (natural log)
  *       block_score  [B][Hkv][max_blocks_per_seq] float32
- *       idx          [B][Hkv][k] int32, ascending block ids, -1 padded
+ *       idx          [B][Hkv][k] int32 selection rows.  Rows the library
+ *                    writes (top-k) hold ascending block ids, -1 padded.
+ *                    Rows it reads (sparse, staged, gather) may hold the
+ *                    ids in any order with padding anywhere: every slot
+ *                    is read, and a slot outside [0, ceil(T_b/128)) names
+ *                    no block.  The ids of a row must be distinct: a
+ *                    repeated id is attended once per repeat.
  *     Query head h uses KV head h / (Hq / Hkv).  Pointers must be 16-byte
  *     aligned.  Every page named by the table holds 128 tokens of storage.
  *   - ctx_lens values are clamped to [0, 128 * max_blocks_per_seq].  A
@@ -110,9 +116,11 @@ hylra_status hylra_block_topk(const hylra_shape *shape, const float *block_score
                               void *hip_stream);
 
 /* Decode attention restricted to the selected blocks (section 2.3, tolerant
- * layers): U = tokens t < T_b whose block id is in idx[b][g][0..k) (negative
- * entries are padding); softmax and output over U only.  An empty U gives
- * out = 0 and lse = -inf.  lse may be NULL. */
+ * layers): U = tokens t < T_b whose block id is one of idx[b][g][0..k), in
+ * any slot (entries outside [0, ceil(T_b/128)), negative ones included, are
+ * padding); softmax and output over U only.  The ids of a row must be
+ * distinct (see the idx layout above).  An empty U gives out = 0 and
+ * lse = -inf.  lse may be NULL.  1 <= k <= 8192 (HYLRA_E_UNSUPPORTED above). */
 hylra_status hylra_decode_sparse(const hylra_shape *shape, const void *q, const hylra_kv *kv,
                                  const int32_t *idx, int32_t k, float *out, float *lse,
                                  void *workspace, size_t workspace_bytes, void *hip_stream);
@@ -127,7 +135,8 @@ hylra_status hylra_decode_sparse(const hylra_shape *shape, const void *q, const 
  * [num_layers][B][Hkv][k] receives the index set each layer computed or
  * reused.  With idx_log NULL, a reset layer whose indices the next layer does
  * not reuse skips the block scores and top-k (nothing would read them).
- * Everything is enqueued on one stream with no host synchronisation. */
+ * Everything is enqueued on one stream with no host synchronisation.
+ * 1 <= k <= 8192 (HYLRA_E_UNSUPPORTED above). */
 hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, const int32_t *src,
                               int32_t k, const void *const *q, const hylra_kv *kv,
                               float *const *out, float *const *lse, int32_t *idx_log,
@@ -147,7 +156,8 @@ hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, cons
  * maps at the same address (hipHostMalloc) or device memory, over their whole
  * extent (num_pages pages); anything else, pageable host memory included, is
  * HYLRA_E_INVALID_ARG.  block_table, ctx_lens, idx and the staging pools are
- * device memory.  B*k <= 2^30. */
+ * device memory.  Every slot r < k of a row is read (idx layout above).
+ * 1 <= k <= 8192, B*k <= 2^30. */
 hylra_status hylra_gather_blocks(const hylra_shape *shape, const hylra_kv *kv, const int32_t *idx,
                                  int32_t k, void *staged_k, void *staged_v, void *hip_stream);
 
@@ -187,7 +197,7 @@ hylra_status hylra_silu_mul(const void *gate_up, void *out, int64_t rows, int32_
  * layer's own pools with the same idx (bit for bit: the same kernel reads the
  * same values in the same order), reading selection slot r of sequence b
  * from staging page b*k + r as hylra_gather_blocks fills it.  ctx_lens [B]
- * is the layer's context lengths; no block table is read. */
+ * is the layer's context lengths; no block table is read.  1 <= k <= 8192. */
 hylra_status hylra_decode_staged(const hylra_shape *shape, const void *q, const void *staged_k,
                                  const void *staged_v, const int32_t *ctx_lens, const int32_t *idx,
                                  int32_t k, float *out, float *lse, void *workspace,
@@ -239,10 +249,13 @@ hylra_status hylra_policy_dp(int32_t num_layers, const float *M, float theta,
  * for the recorded events and returns the summed kernel time in milliseconds
  * and the number of timed launches (both pointers nullable).  Timers are
  * process-global and not thread-safe; starting a running timer restarts it. */
-#define HYLRA_KERNEL_FULL_ATTN 0   /* full attention layer: split pass + merge, scores, top-k */
+#define HYLRA_KERNEL_FULL_ATTN 0   /* full attention layer without block scores: split pass + merge */
 #define HYLRA_KERNEL_SPARSE_ATTN 1 /* selected-block attention layer: split pass + merge */
 #define HYLRA_KERNEL_TOPK 2        /* top-k of a given score array (hylra_block_topk) */
 #define HYLRA_KERNEL_GATHER 3      /* selected-block gather (hylra_gather_blocks, offloading) */
+#define HYLRA_KERNEL_FULL_ATTN_SCORED 4 /* full attention layer with block scores, and the
+                                           top-k when the index set is used: split pass +
+                                           merge, scores, top-k */
 hylra_status hylra_timer_start(int32_t kind, int32_t capacity);
 hylra_status hylra_timer_stop(int32_t kind, double *total_ms, int32_t *launches);
 

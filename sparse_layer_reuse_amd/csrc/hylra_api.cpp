@@ -77,6 +77,15 @@ hylra_status check_kv(const hylra_kv *kv) {
   return HYLRA_OK;
 }
 
+// Length of a selection row: 1 <= k <= kMaxBlocks (every slot of a row is
+// walked, so k also bounds the work of a launch).
+hylra_status check_k(int k) {
+  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (k > hylra::kMaxBlocks)
+    return fail(HYLRA_E_UNSUPPORTED, "k must be <= %d (got %d)", hylra::kMaxBlocks, k);
+  return HYLRA_OK;
+}
+
 float logit_scale_log2(const hylra_shape *s) {
   const float scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
   return scale * 1.4426950408889634f;
@@ -286,6 +295,10 @@ hylra_status check_staging(const void *k_pool, const void *v_pool) {
 
 namespace hylra {
 
+int report_error(int status, const char *message) {
+  return fail(status, "%s", message);
+}
+
 // Split plans: about 256 workgroups per launch (one 8-wavefront workgroup
 // resident per compute unit on a 256-CU part) and at most kMaxWgChunks chunks
 // per workgroup.  Full mode: a multiple of 8 chunks per workgroup (one per
@@ -317,11 +330,11 @@ SplitPlan plan_full(int batch, int num_kv_heads, int max_blocks) {
 
 SplitPlan plan_sparse(int batch, int num_kv_heads, int max_blocks, int k, int group,
                       int head_dim) {
-  const long keff = k < max_blocks ? k : max_blocks;
+  (void)max_blocks;  // every one of the k selection slots is walked
   const long items = (long)group * head_dim / 4;  // merge threads per split
   long max_splits = 8 * (items < 512 ? 512 / items : 1);
   if (max_splits > kMaxSplits) max_splits = kMaxSplits;
-  return make_plan((long)kChunksPerBlock * (keff > 0 ? keff : 1), (long)batch * num_kv_heads,
+  return make_plan((long)kChunksPerBlock * (k > 0 ? k : 1), (long)batch * num_kv_heads,
                    (long)kChunksPerBlock, max_splits);
 }
 
@@ -376,7 +389,7 @@ hylra_status hylra_decode_sparse(const hylra_shape *shape, const void *q, const 
   if (q == nullptr || out == nullptr || idx == nullptr)
     return fail(HYLRA_E_INVALID_ARG, "q, idx and out must be non-NULL");
   if (!aligned16(q) || !aligned16(out)) return fail(HYLRA_E_INVALID_ARG, "q and out must be 16-byte aligned");
-  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (hylra_status st = check_k(k)) return st;
   Workspace w;
   if (hylra_status st = check_ws(shape, k, workspace, workspace_bytes, w)) return st;
   if (hylra_status st = run_sparse(shape, q, kv, idx, k, out, lse, nullptr, w, hip_stream))
@@ -392,7 +405,7 @@ hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, cons
   if (num_layers < 1) return fail(HYLRA_E_INVALID_ARG, "num_layers must be >= 1");
   if (src == nullptr || q == nullptr || kv == nullptr || out == nullptr)
     return fail(HYLRA_E_INVALID_ARG, "src, q, kv and out must be non-NULL");
-  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (hylra_status st = check_k(k)) return st;
   if (src[0] != 0) return fail(HYLRA_E_BAD_POLICY, "layer 0 must reset (src[0] = %d)", src[0]);
   for (int j = 1; j < num_layers; ++j)
     if (src[j] != j && src[j] != src[j - 1])
@@ -430,7 +443,7 @@ hylra_status hylra_gather_blocks(const hylra_shape *shape, const hylra_kv *kv, c
   if (hylra_status st = check_shape(shape)) return st;
   if (hylra_status st = check_kv(kv)) return st;
   if (idx == nullptr) return fail(HYLRA_E_INVALID_ARG, "idx must be non-NULL");
-  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (hylra_status st = check_k(k)) return st;
   if ((long)shape->batch * k > (1L << 30))
     return fail(HYLRA_E_UNSUPPORTED, "batch * k = %ld exceeds 2^30 staging pages", (long)shape->batch * k);
   if (hylra_status st = check_staging(staged_k, staged_v)) return st;
@@ -513,7 +526,7 @@ hylra_status hylra_decode_staged(const hylra_shape *shape, const void *q, const 
   if (q == nullptr || out == nullptr || idx == nullptr || ctx_lens == nullptr)
     return fail(HYLRA_E_INVALID_ARG, "q, ctx_lens, idx and out must be non-NULL");
   if (!aligned16(q) || !aligned16(out)) return fail(HYLRA_E_INVALID_ARG, "q and out must be 16-byte aligned");
-  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (hylra_status st = check_k(k)) return st;
   if ((long)shape->batch * k > (1L << 30))
     return fail(HYLRA_E_UNSUPPORTED, "batch * k = %ld exceeds 2^30 staging pages", (long)shape->batch * k);
   Workspace w;
@@ -535,7 +548,7 @@ hylra_status hylra_run_policy_offload(const hylra_shape *shape, int32_t num_laye
   if (num_layers < 1) return fail(HYLRA_E_INVALID_ARG, "num_layers must be >= 1");
   if (src == nullptr || q == nullptr || kv == nullptr || out == nullptr || offloaded == nullptr)
     return fail(HYLRA_E_INVALID_ARG, "src, q, kv, offloaded and out must be non-NULL");
-  if (k < 1) return fail(HYLRA_E_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (hylra_status st = check_k(k)) return st;
   if ((long)shape->batch * k > (1L << 30))
     return fail(HYLRA_E_UNSUPPORTED, "batch * k = %ld exceeds 2^30 staging pages", (long)shape->batch * k);
   if (src[0] != 0) return fail(HYLRA_E_BAD_POLICY, "layer 0 must reset (src[0] = %d)", src[0]);

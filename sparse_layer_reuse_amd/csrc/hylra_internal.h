@@ -143,14 +143,18 @@ struct OverlapArgs {
 size_t overlap_smem_bytes(int layers, int k);
 int launch_overlap(const OverlapArgs &a, void *stream);
 const char *device_error_string(int code);
+// Records `message` as the calling thread's last error (hylra_last_error) and
+// returns `status`.
+int report_error(int status, const char *message);
 
 // Kernel timers (see hylra_timer_start in hylra.h).
 enum TimerKind {
-  kTimerFullAttn = 0,
+  kTimerFullAttn = 0,    // full attention, no block scores
   kTimerSparseAttn = 1,
   kTimerTopk = 2,
   kTimerGather = 3,
-  kNumTimers = 4
+  kTimerFullScored = 4,  // full attention with block scores (and the top-k when asked)
+  kNumTimers = 5
 };
 int timer_start(int kind, int capacity);
 int timer_stop(int kind, double *total_ms, int *launches);

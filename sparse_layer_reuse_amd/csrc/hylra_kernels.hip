@@ -86,11 +86,12 @@ __device__ __forceinline__ int clamp_ctx(int t, int max_blocks) {
 }
 
 // Number of 32-token chunk positions of (b, g) in a launch.  Full: every chunk
-// of the context.  Sparse: four per selected block (k_eff = min(k, N_b)).
+// of the context.  Sparse: four per selection slot, for all k slots of the row
+// (a slot holding no block of the context resolves to an empty chunk), so
+// the ids of a row may sit in any order with padding anywhere.
 __device__ __forceinline__ int chunk_positions(int T, const int32_t *sel, int k) {
   if (sel == nullptr) return (T + kChunkTokens - 1) / kChunkTokens;
-  const int nb = (T + kBlockTokens - 1) / kBlockTokens;
-  return kChunksPerBlock * (k < nb ? k : nb);
+  return T > 0 ? kChunksPerBlock * k : 0;
 }
 
 // Resolves chunk position `pos` of (b, g) to its page and the valid tokens
@@ -1238,7 +1239,8 @@ int timer_stop(int kind, double *total_ms, int *launches) {
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream) {
   const dim3 grid(a.nsplit, a.num_kv_heads, batch);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const TimerScope tm(a.sel == nullptr ? kTimerFullAttn : kTimerSparseAttn);
+  const TimerScope tm(a.sel != nullptr ? kTimerSparseAttn
+                      : a.stats != nullptr ? kTimerFullScored : kTimerFullAttn);
   const dim3 block(kThreads);
 #define HYLRA_LAUNCH(K) hipExtLaunchKernelGGL(K, grid, block, 0, st, tm.start, tm.stop, 0, a)
   const bool staged = a.staged != 0;

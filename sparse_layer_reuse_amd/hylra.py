@@ -90,9 +90,10 @@ EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
             "hylra_status_str",
             "hylra_last_error")
 
-KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_TOPK, KERNEL_GATHER = range(4)
+KERNEL_FULL_ATTN, KERNEL_SPARSE_ATTN, KERNEL_TOPK, KERNEL_GATHER, KERNEL_FULL_SCORED = range(5)
 KERNEL_NAMES = {KERNEL_FULL_ATTN: "attn_full_layer", KERNEL_SPARSE_ATTN: "attn_sparse_layer",
-                KERNEL_TOPK: "score_topk", KERNEL_GATHER: "gather_blocks"}
+                KERNEL_TOPK: "score_topk", KERNEL_GATHER: "gather_blocks",
+                KERNEL_FULL_SCORED: "attn_full_layer_scored"}
 
 
 def _status_str(st: int) -> str:

@@ -4,8 +4,10 @@ same seeded inputs.
 Bars: float32 K/V -> max |err| <= 1e-5 on out and lse; bfloat16 K/V with
 float32 accumulation -> max |err| <= 2e-3.  Top-k indices bit-exact, except
 for a (sequence, KV head) whose oracle cut margin (k-th vs (k+1)-th block
-score, relative) is below 1e-5; there the reuse layers are checked with the
-GPU's index set fed to the oracle.
+score, relative) is below 1e-5: there the GPU row must still be well formed
+and differ from the oracle's only by blocks inside the 1e-5 tie window
+(oracle/acceptance.py), and the reuse layers are checked with the GPU's
+index set fed to the oracle.
 """
 import math
 
@@ -14,12 +16,12 @@ import pytest
 import torch
 
 import oracle
+from oracle.acceptance import check_topk_rows
 from sparse_layer_reuse_amd import synth, workloads as W
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-3}
-MARGIN = 1e-5
 
 
 @pytest.fixture(scope="module")
@@ -209,6 +211,44 @@ def test_decode_sparse_all_blocks_equals_full(H):
     assert (lse_s - lse_f).abs().max().item() <= 1e-5
 
 
+def test_decode_sparse_any_slot_order(H):
+    """Selection rows read by the sparse path may hold their ids in any order
+    with padding anywhere: front padding, ids out of order, ids past the
+    context and past the table, negative padding other than -1, and a row
+    that is all padding.  The oracle reads each row as a set."""
+    ctx = (2000, 700, 128)
+    Hq, Hkv, d, k = 16, 4, 128, 7
+    say("decode_sparse any slot order", ctx, k)
+    lay = gpu_layer("bf16", ctx, Hq, Hkv, d, seed=41, max_blocks=20)
+    sel = np.full((3, Hkv, k), -1, np.int32)
+    sel[0, 0] = [-1, -1, 9, 3, 15, -1, 0]       # front padding, out of order
+    sel[0, 1] = [15, 14, 13, 12, 11, 10, 1]     # descending
+    sel[0, 2] = [-5, 16, 2, 40, -1, 7, 100]     # past the context (16 blocks) and the table (20)
+    sel[0, 3] = [-1] * k                        # empty selection
+    sel[1, 0] = [5, -1, 4, -1, 3, 2, 1]         # N = 6 for 700 tokens
+    sel[1, 1] = [6, 7, 8, 0, -2, -3, -4]        # ids >= N are padding
+    sel[1, 2] = [0, 1, 2, 3, 4, 5, -1]          # every block, padding last
+    sel[1, 3] = [-1, -1, -1, -1, -1, -1, 5]     # one id in the last slot
+    sel[2] = [-1, 0, -1, -1, -1, -1, -1]        # one-block sequence
+    o0, l0 = nan_out(lay["q"])
+    out, lse = H.decode_sparse(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"],
+                               torch.from_numpy(sel).cuda(), out=o0, lse=l0)
+    assert counters_are_zero(H, lay["q"], lay["k_pool"], lay["table"], k)
+    o = synth.layer_to_oracle(lay)
+    r_out, r_lse, _ = oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
+                                    num_kv_heads=Hkv, sel=sel, k=k)
+    assert_close(out.cpu().numpy(), r_out, TOL["bf16"], "out")
+    assert_close(lse.cpu().numpy(), r_lse, TOL["bf16"], "lse")
+    # the same sets sorted ascending with padding last give the same result
+    srt = np.sort(np.where((sel >= 0) & (sel < 20), sel, 1 << 30), axis=-1)
+    srt = np.where(srt == 1 << 30, -1, srt).astype(np.int32)
+    out2, lse2 = H.decode_sparse(lay["q"], lay["k_pool"], lay["v_pool"], lay["table"],
+                                 lay["ctx"], torch.from_numpy(srt).cuda())
+    torch.cuda.synchronize()
+    assert_close(out2.cpu().numpy(), out.cpu().numpy(), 1e-5, "sorted rows, out")
+    assert_close(lse2.cpu().numpy(), lse.cpu().numpy(), 1e-5, "sorted rows, lse")
+
+
 def sampled_sequences(layer, seqs):
     """Oracle inputs for a subset of a layer's sequences: their q rows and
     context lengths, and only the pages their block-table rows name, gathered
@@ -252,13 +292,12 @@ def check_policy_run(H, layers_gpu, src, k, dtype, num_kv_heads, check_layers=No
         if src[j] == j:
             r_out, r_lse, score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"],
                                                      o["ctx"], num_kv_heads=num_kv_heads)
-            carried, margin = oracle.topk(score, o["ctx"], k)
-            near = margin < MARGIN
-            same = np.all(idx_gpu[j] == carried, axis=-1)
-            assert np.all(same | near), "layer %d: top-k differs away from a near-tie" % j
-            if near.any():
-                say("layer", j, "near-tie rows excused:", int(near.sum()))
-                carried = np.where(same[..., None], carried, idx_gpu[j])
+            want, margin = oracle.topk(score, o["ctx"], k)
+            excused = check_topk_rows(idx_gpu[j], want, score, margin, o["ctx"], k,
+                                      what="layer %d" % j)
+            if excused:
+                say("layer", j, "near-tie rows excused:", excused)
+            carried = idx_gpu[j].copy()
         else:
             assert np.array_equal(idx_gpu[j], idx_gpu[src[j]]), "layer %d: carried set" % j
             r_out, r_lse, _ = oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"],
@@ -307,17 +346,16 @@ def test_run_policy_k_covering_everything_equals_full(H):
         assert (l - fl).abs().max().item() <= 1e-5
 
 
-def test_run_policy_llama3_8b_32k_sampled(H):
-    """Full-size 8B-shaped workload (32 layers, 32K context) in the benchmark's
-    launch configuration; the oracle checks a sample of layers."""
+def test_run_policy_llama3_8b_32k_all_layers(H):
+    """Full-size 8B-shaped workload (32 layers, 32K context, batch 1) in the
+    benchmark's launch configuration; the oracle checks every layer."""
     wl = W.LLAMA3_8B_32K
-    say("run_policy", wl.name, "full size, sampled layers")
+    say("run_policy", wl.name, "full size, all layers")
     layers = synth.workload_layers(wl, device="cuda")
     src = W.src_from_resets(wl.layers, wl.resets)
-    check = [0, 3, 4, 5, 7, 13, 28, 31]
     n, outs, lses, idx_log = check_policy_run(H, layers, src, wl.topk[0], wl.dtype,
-                                              wl.num_kv_heads, check_layers=check)
-    assert n == len(check)
+                                              wl.num_kv_heads)
+    assert n == wl.layers
     # determinism of the whole step
     outs2, lses2, idx2 = H.run_policy(layers, src, wl.topk[0])
     torch.cuda.synchronize()
@@ -457,9 +495,7 @@ def test_merge_instances_full_with_topk(H, G, nsplit):
     assert_close(outs[0].cpu().numpy(), r_out, TOL["bf16"], "out")
     assert_close(lses[0].cpu().numpy(), r_lse, TOL["bf16"], "lse")
     want, margin = oracle.topk(r_score, o["ctx"], k)
-    got = idx_log[0].cpu().numpy()
-    near = margin < MARGIN
-    assert np.all(np.all(got == want, axis=-1) | near), (got, want)
+    check_topk_rows(idx_log[0].cpu().numpy(), want, r_score, margin, o["ctx"], k)
 
 
 @pytest.mark.parametrize("G,k", [(4, 2), (4, 16), (4, 40), (8, 2), (8, 8), (8, 30),
@@ -496,8 +532,7 @@ def test_merge_generic_instance_d64_many_splits(H):
     assert_close(outs[0].cpu().numpy(), r_out, TOL["bf16"], "out")
     assert_close(lses[0].cpu().numpy(), r_lse, TOL["bf16"], "lse")
     want, margin = oracle.topk(r_score, o["ctx"], k)
-    got = idx_log[0].cpu().numpy()
-    assert np.all(np.all(got == want, axis=-1) | (margin < MARGIN))
+    check_topk_rows(idx_log[0].cpu().numpy(), want, r_score, margin, o["ctx"], k)
 
 
 # Full mode merges in two levels when one (sequence, KV head) has more than
