@@ -142,6 +142,24 @@ hylra_status hylra_run_policy(const hylra_shape *shape, int32_t num_layers, cons
                               float *const *out, float *const *lse, int32_t *idx_log,
                               void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* hylra_run_policy for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, with the workspace taken from a static device
+ * array of HYLRA_NOALLOC_SCRATCH_BYTES inside the library instead of a
+ * caller buffer.  The caller still passes inputs and outputs.  Each device
+ * holds its own array from its first call until the process ends; the first
+ * call on a device looks the array up and clears its counters on hip_stream.
+ * The entry point allocates and frees nothing.  A shape whose
+ * hylra_workspace_size exceeds the array returns HYLRA_E_WORKSPACE (nothing
+ * enqueued).  Every call on one device shares that device's array, so calls
+ * that overlap on one device (several streams or host threads) race; run
+ * them in order on one stream. */
+#define HYLRA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+hylra_status hylra_run_policy_noalloc(const hylra_shape *shape, int32_t num_layers,
+                                      const int32_t *src, int32_t k, const void *const *q,
+                                      const hylra_kv *kv, float *const *out, float *const *lse,
+                                      int32_t *idx_log, void *hip_stream);
+
 /* Index-guided offloading (section 2.4, hardware-efficient optimisations):
  * the indices a reuse layer carries name, before it runs, the only blocks it
  * reads, so its KV cache can stay in host memory and just those blocks cross

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhylra.so")
 SOURCES = ["hylra_kernels.hip", "hylra_profile.hip", "hylra_offload.hip", "hylra_step.hip",
-           "hylra_api.cpp"]
+           "hylra_noalloc.hip", "hylra_api.cpp"]
 ARCH = os.environ.get("HYLRA_OFFLOAD_ARCH", "gfx950")
 COMPILE_TIMEOUT_S = 900  # a stuck compiler fails the build instead of hanging it
 

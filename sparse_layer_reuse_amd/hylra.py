@@ -68,6 +68,7 @@ def _load():
         "hylra_silu_mul": [P, P, ctypes.c_int64, I32, P],
         "hylra_decode_staged": [SP, P, P, P, P, P, I32, P, P, P, SZ, P],
         "hylra_run_policy_offload": [SP, I32, P, I32, P, KP, P, P, P, P, P, P, P, SZ, P, P],
+        "hylra_run_policy_noalloc": [SP, I32, P, I32, P, KP, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -86,7 +87,7 @@ EXPORTED = ("hylra_workspace_size", "hylra_decode_full", "hylra_block_topk",
             "hylra_decode_sparse", "hylra_run_policy", "hylra_policy_dp", "hylra_timer_start",
             "hylra_timer_stop", "hylra_overlap_matrix", "hylra_read_probe", "hylra_gather_blocks",
             "hylra_decode_staged", "hylra_run_policy_offload", "hylra_append_kv",
-            "hylra_rope_append", "hylra_silu_mul",
+            "hylra_rope_append", "hylra_silu_mul", "hylra_run_policy_noalloc",
             "hylra_status_str",
             "hylra_last_error")
 
@@ -390,6 +391,19 @@ class PolicyPlan:
                                      _ptr(self.idx_log), _ptr(self.ws), self.ws.numel(),
                                      _stream(stream)))
         return self.out, self.lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # HYLRA_NOALLOC_SCRATCH_BYTES
+
+
+def run_policy_noalloc(plan: PolicyPlan, stream=None):
+    """hylra_run_policy_noalloc on a plan's pre-marshalled arguments: the same
+    step as plan.run(), with the library's static device scratch in place of
+    the plan's workspace.  Returns (outs, lses)."""
+    _check(_lib.hylra_run_policy_noalloc(ctypes.byref(plan.shape), plan.L, plan.src, plan.k,
+                                         plan.qs, plan.kvs, plan.outs, plan.lses,
+                                         _ptr(plan.idx_log), _stream(stream)))
+    return plan.out, plan.lse
 
 
 class OffloadPlan(PolicyPlan):
