@@ -73,6 +73,10 @@ def parse():
                    help="time only the hybrid step (for short profiler runs)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only copy a MIB-sized buffer 4 times (calibrates HBM byte counters)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the 64K-128K workloads of the `configs` object (headline only)")
+    p.add_argument("--config-steps", type=int, default=10,
+                   help="timed steps per policy of the `configs` workloads")
     return p.parse_args()
 
 
@@ -297,6 +301,145 @@ def cpu_baseline(wl, layers, src, k, budget_s):
         "reuse_layer_s": mean(t_reuse),
         "single_core": single,
     }
+
+
+def host_cpu():
+    """Model name and socket count of the host CPU (from /proc/cpuinfo)."""
+    model, sockets = None, set()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key == "model name" and model is None:
+                    model = val.strip()
+                elif key == "physical id":
+                    sockets.add(val.strip())
+    except OSError:
+        pass
+    return {"cpu_model": model, "sockets": len(sockets) or None,
+            "logical_cpus": os.cpu_count()}
+
+
+def oracle_layer_times(wl, layers, src, k):
+    """Oracle (all host threads) on one reset layer and one reuse layer of the
+    workload (the reuse layer attends the reset layer's top-k set): seconds
+    per reset layer and per reuse layer."""
+    import oracle
+    from sparse_layer_reuse_amd import synth
+    reset_j = 0
+    reuse_j = next((j for j, s_ in enumerate(src) if s_ != j), None)
+    o = synth.layer_to_oracle(layers[reset_j])
+    t0 = time.perf_counter()
+    _, _, score = oracle.decode_full(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
+                                     num_kv_heads=wl.num_kv_heads)
+    sel, _ = oracle.topk(score, o["ctx"], k)
+    t_reset = time.perf_counter() - t0
+    del o, score
+    t_reuse = None
+    if reuse_j is not None:
+        o = synth.layer_to_oracle(layers[reuse_j])
+        t0 = time.perf_counter()
+        oracle.attend(o["q"], o["k_pool"], o["v_pool"], o["table"], o["ctx"],
+                      num_kv_heads=wl.num_kv_heads, sel=sel, k=k)
+        t_reuse = time.perf_counter() - t0
+        del o
+    return t_reset, t_reuse
+
+
+def measure_policy(layers, src, k, steps, warmup, torch, hylra, full_bytes, sparse_bytes):
+    """One policy on resident layers: graph-replayed steps/s and the average
+    launch time of each kernel kind (events stamped by the launches) with its
+    fraction of the HBM peak."""
+    plan = hylra.PolicyPlan(layers, src, k)
+    kinds = (hylra.KERNEL_FULL_SCORED, hylra.KERNEL_FULL_ATTN, hylra.KERNEL_SPARSE_ATTN)
+    _, kern = timed(plan.run, steps, warmup, torch, kinds, hylra)
+    ms, g = graph_timed(plan.run, steps, warmup, torch)
+    del g, plan
+    us = lambda kind: kern[kind][0] * 1e3 if kern[kind][0] is not None else None
+    frac = lambda b, t: b / (t * 1e-6) / 1e9 / HBM_PEAK_GBS if t else None
+    resets = sum(1 for j, s_ in enumerate(src) if s_ == j)
+    return {
+        "resets": resets, "reuses": len(src) - resets,
+        "steps_per_s": 1000.0 / ms, "ms_per_step": ms,
+        "reset_with_topk_us": us(hylra.KERNEL_FULL_SCORED),
+        "reset_without_topk_us": us(hylra.KERNEL_FULL_ATTN),
+        "reuse_us": us(hylra.KERNEL_SPARSE_ATTN),
+        "frac_reset_with_topk": frac(full_bytes, us(hylra.KERNEL_FULL_SCORED)),
+        "frac_reset_without_topk": frac(full_bytes, us(hylra.KERNEL_FULL_ATTN)),
+        "frac_reuse": frac(sparse_bytes, us(hylra.KERNEL_SPARSE_ATTN)),
+    }
+
+
+def measure_configs(args, torch, hylra):
+    """The 64K-128K workloads of the metric beside the headline: for each,
+    the full-attention step and every policy it is quoted with (the DP
+    thresholds or the top-k sweep, and static Jump-3 / Jump-4 policies for
+    the DP workloads), each as graph-replayed steps/s with per-kernel launch
+    times and fractions of the HBM peak; plus the oracle on one reset and
+    one reuse layer of the workload, scaled to the policy's layer counts
+    (labelled extrapolated)."""
+    from sparse_layer_reuse_amd import synth, workloads as W
+    plans = [
+        ("llama3_8b_b8_64k_dp", [("dp", 0.8, 32), ("jump", 3, 32), ("jump", 4, 32)]),
+        ("llama3_8b_paged_128k", [("fixed", None, 8), ("fixed", None, 32), ("fixed", None, 64)]),
+        ("llama3_70b_128k_dp", [("dp", 0.7, 32), ("dp", 0.8, 32), ("dp", 0.9, 32),
+                                ("jump", 3, 32), ("jump", 4, 32)]),
+    ]
+    steps, warmup = args.config_steps, 3
+    out = {}
+    for name, policies in plans:
+        wl = W.get(name)
+        t0 = time.time()
+        layers = synth.workload_layers(wl, device="cuda")
+        torch.cuda.synchronize()
+        gen_s = time.time() - t0
+        full_bytes = wl.kv_bytes_per_layer()
+        full = hylra.FullPlan(layers)
+        _, kf = timed(full.run, steps, warmup, torch, (hylra.KERNEL_FULL_ATTN,), hylra)
+        ms_full, g = graph_timed(full.run, steps, warmup, torch)
+        del g, full
+        full_us = kf[hylra.KERNEL_FULL_ATTN][0] * 1e3
+        entry = {
+            "batch": wl.batch, "layers": wl.layers, "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads, "ctx": wl.ctx, "paged": wl.paged,
+            "kv_bytes_per_layer": full_bytes, "input_generation_s": gen_s,
+            "full_steps_per_s": 1000.0 / ms_full, "full_layer_us": full_us,
+            "frac_full_layer": full_bytes / (full_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "policies": {},
+        }
+        oracle_t = None
+        for kind, param, k in policies:
+            if kind == "jump":
+                src = W.src_from_resets(wl.layers, range(0, wl.layers, param))
+                label = "jump%d_k%d" % (param, k)
+            elif kind == "dp":
+                M = synth.workload_similarity(wl)
+                force = [j in wl.dp_force for j in range(wl.layers)]
+                src, _, _ = hylra.policy_dp(M, param, force)
+                label = "dp_theta%g_k%d" % (param, k)
+            else:
+                src = W.src_from_resets(wl.layers, wl.resets)
+                label = "fixed_k%d" % k
+            sparse_bytes = full_bytes * min(k, wl.blocks) // wl.blocks
+            r = measure_policy(layers, src, k, steps, warmup, torch, hylra, full_bytes,
+                               sparse_bytes)
+            r["hybrid_over_full"] = r["steps_per_s"] / entry["full_steps_per_s"]
+            if args.cpu_seconds > 0:
+                if oracle_t is None or oracle_t[2] != k:
+                    tr, tu = oracle_layer_times(wl, layers, src, k)
+                    oracle_t = (tr, tu, k)
+                tr, tu = oracle_t[0], oracle_t[1]
+                step_s = r["resets"] * tr + r["reuses"] * (tu or 0.0)
+                r["cpu_oracle_extrapolated"] = {
+                    "steps_per_s": 1.0 / step_s, "reset_layer_s": tr, "reuse_layer_s": tu,
+                    "note": "extrapolated: one reset and one reuse layer timed, scaled by "
+                            "the policy's layer counts"}
+            entry["policies"][label] = r
+        out[name] = entry
+        del layers
+        torch.cuda.empty_cache()
+    return out
 
 
 def e2e(args, wl, k, src, policy_desc):
@@ -570,8 +713,13 @@ def main():
         out["roofline"]["frac_of_stream_ceiling"] = achieved / ceil["gbs"]
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(wl, layers, src, k, args.cpu_seconds)
+        out["cpu_baseline"].update(host_cpu())
     else:
         out["cpu_baseline"] = None
+    if not args.no_configs and wl.name == "llama3_8b_32k" and L == wl.layers:
+        del hybrid, layers
+        torch.cuda.empty_cache()
+        out["configs"] = measure_configs(args, torch, hylra)
     print(json.dumps(out), flush=True)
 
 

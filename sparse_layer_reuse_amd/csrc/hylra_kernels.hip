@@ -11,17 +11,20 @@
 //                of the KV head; the eight states are merged in LDS and written
 //                as the workgroup's partial.  bf16 K/V: q.K and p.V on MFMA
 //                (v_mfma_f32_16x16x32_bf16); float32 K/V: vector ALU.
-//                Full mode walks every chunk of the sequence, sparse mode the
+//                Full modes walk every chunk of the sequence, sparse modes the
 //                chunks of the selected blocks through the block table.  The
 //                chunks are dealt round-robin (wavefront w takes w, w+8, ...),
 //                so the eight wavefronts stream neighbouring chunks together.
-//                Full mode records each chunk's softmax mass; a block's four
-//                chunk masses are summed when the partial is written.
+//                The scored mode records each chunk's softmax mass; a block's
+//                four chunk masses are summed when the partial is written.
 //   epilogue     the last workgroup of a (sequence, KV head) to finish (device
 //                scope arrival counter; partials handed over with coherent
 //                device-scope stores and loads) merges them into out / lse and,
-//                in full mode, turns the block masses into block scores and
-//                selects the top-k blocks (radix select, lower id wins ties).
+//                in scored mode, turns the block masses into block scores and
+//                selects the top-k blocks (one wavefront, lower id wins ties)
+//                while its other wavefronts merge the output.
+// The mode (full, scored, sparse, staged) is a template argument: each
+// launch runs an instance holding only its own code.
 // A separate small kernel selects the top-k of a caller-given score array.
 //
 // Softmax state is kept in base 2: x = s * scale * log2(e), p = 2^(x - m).
@@ -85,40 +88,88 @@ __device__ __forceinline__ int clamp_ctx(int t, int max_blocks) {
   return t < 0 ? 0 : (t > max_blocks * kBlockTokens ? max_blocks * kBlockTokens : t);
 }
 
+// Launch modes of the attention kernel (compile-time, one instance each):
+//   full     reset layer whose index set nobody reads: split pass + merge
+//   scored   reset layer: split pass recording block masses + merge, block
+//            scores and the top-k selection
+//   sparse   reuse layer: the selected blocks through the block table
+//   staged   reuse layer: the selected blocks from a staging pool
+constexpr int kModeFull = 0;
+constexpr int kModeScored = 1;
+constexpr int kModeSparse = 2;
+constexpr int kModeStaged = 3;
+constexpr bool mode_sparse(int mode) { return mode == kModeSparse || mode == kModeStaged; }
+
 // Number of 32-token chunk positions of (b, g) in a launch.  Full: every chunk
 // of the context.  Sparse: four per selection slot, for all k slots of the row
 // (a slot holding no block of the context resolves to an empty chunk), so
 // the ids of a row may sit in any order with padding anywhere.
-__device__ __forceinline__ int chunk_positions(int T, const int32_t *sel, int k) {
-  if (sel == nullptr) return (T + kChunkTokens - 1) / kChunkTokens;
-  return T > 0 ? kChunksPerBlock * k : 0;
+template <int kMode>
+__device__ __forceinline__ int chunk_positions(int T, int k) {
+  if constexpr (mode_sparse(kMode)) return T > 0 ? kChunksPerBlock * k : 0;
+  return (T + kChunkTokens - 1) / kChunkTokens;
 }
 
 // Resolves chunk position `pos` of (b, g) to its page and the valid tokens
 // (all arguments wavefront-uniform).  Returns false when the chunk holds no
 // token to read: past the context, a padding / out-of-range selected id, or a
-// page outside the pool.
-// kStaged: the pools are a staging pool (selection slot r of sequence b in
-// page b * k + r) and no block table is read.  A compile-time choice: a
-// run-time flag in this code slows the regular kernels' selected-block path.
-template <bool kStaged>
+// page outside the pool.  Staged mode: the pools are a staging pool
+// (selection slot r of sequence b in page b * k + r) and no block table is
+// read.
+template <int kMode>
 __device__ __forceinline__ bool resolve_chunk(const AttnArgs &a, int b, int g, int T, int pos,
                                               int &page, int &sub, int &valid) {
   int n;
-  if (a.sel == nullptr) {
-    n = pos / kChunksPerBlock;
-  } else {
+  if constexpr (mode_sparse(kMode)) {
     n = scalar_load(a.sel, ((int64_t)b * a.num_kv_heads + g) * a.k + pos / kChunksPerBlock);
     if (n < 0 || n >= (T + kBlockTokens - 1) / kBlockTokens) return false;
+  } else {
+    n = pos / kChunksPerBlock;
   }
   sub = pos % kChunksPerBlock;
   valid = T - (n * kBlockTokens + sub * kChunkTokens);
   if (valid <= 0) return false;
   if (valid > kChunkTokens) valid = kChunkTokens;
-  if constexpr (kStaged)
+  if constexpr (kMode == kModeStaged)
     page = b * a.k + pos / kChunksPerBlock;
   else
     page = scalar_load(a.table, (int64_t)b * a.max_blocks + n);
+  return page >= 0 && page < a.num_pages;
+}
+
+// Block id and page of a wavefront's first chunk (position pos), loaded at
+// the start of the kernel together with the context length: neither load
+// depends on it, so the first K/V loads wait for one round trip less.  Out
+// of range ids give n = -1 / page = -1; resolve_first then checks them
+// against the context as resolve_chunk does.
+struct FirstChunk {
+  int n, page;
+};
+template <int kMode>
+__device__ __forceinline__ FirstChunk prefetch_first(const AttnArgs &a, int b, int g, int pos) {
+  FirstChunk f{-1, -1};
+  if constexpr (mode_sparse(kMode)) {
+    if (pos < kChunksPerBlock * a.k)
+      f.n = scalar_load(a.sel, ((int64_t)b * a.num_kv_heads + g) * a.k + pos / kChunksPerBlock);
+  } else {
+    f.n = pos / kChunksPerBlock;
+  }
+  if constexpr (kMode != kModeStaged) {
+    if (f.n >= 0 && f.n < a.max_blocks) f.page = scalar_load(a.table, (int64_t)b * a.max_blocks + f.n);
+  } else {
+    f.page = b * a.k + pos / kChunksPerBlock;
+  }
+  return f;
+}
+template <int kMode>
+__device__ __forceinline__ bool resolve_first(const AttnArgs &a, int T, int pos, FirstChunk f,
+                                              int &page, int &sub, int &valid) {
+  if (f.n < 0 || f.n >= (T + kBlockTokens - 1) / kBlockTokens) return false;
+  sub = pos % kChunksPerBlock;
+  valid = T - (f.n * kBlockTokens + sub * kChunkTokens);
+  if (valid <= 0) return false;
+  if (valid > kChunkTokens) valid = kChunkTokens;
+  page = f.page;
   return page >= 0 && page < a.num_pages;
 }
 
@@ -216,6 +267,13 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
+// The last workgroup of a reset layer splits its wavefronts in two groups
+// after the per-head statistics: wavefronts [0, kScoreWaves) compute the
+// block scores and wavefront 0 then selects the top-k; the others merge the
+// output partials at the same time.
+constexpr int kScoreWaves = 4;
+constexpr int kScoreThreads = 64 * kScoreWaves;
+
 // LDS of the split pass: the wavefront states and the chunk masses.
 template <int D>
 struct SplitSmem {
@@ -226,69 +284,65 @@ struct SplitSmem {
   float cp[kMaxWgChunks][kMaxGroup];  // chunk: its softmax mass relative to cm
 };
 
-// LDS used by the epilogue and the top-k selection.
+// LDS of the one-wavefront top-k selection.
+struct SelectSmem {
+  uint32_t cand_key[256];  // candidates of the filter, in ascending block id
+  int32_t cand_id[256];
+  int hist[256];           // digit histogram of the radix fallback
+};
+
+// LDS used by the epilogue.
 struct EpiSmem {
   float f[kMaxGroup][kMaxSplits];  // per (head, split) rescale factor 2^(m_s - M)
   float f2[kMaxGroup][kMaxGroups]; // two-level: per (head, group) factor 2^(m_q - M)
   float M[kMaxGroup];
   float L[kMaxGroup];
   float invL[kMaxGroup];
-  f32x4 red[kThreads];
-  uint32_t keys[kMaxBlocks];
-  int hist[4][kWaves][256];  // top-k digit histograms (one set per radix pass, per wavefront)
-  uint32_t kor[kWaves], kand[kWaves];
-  int seg_gt[kWaves], seg_eq[kWaves];
+  uint32_t keys[kMaxBlocks];       // block score bits (scores >= 0 order as unsigned)
+  SelectSmem sel;
 };
 
-// Top-k preparation, done by every thread while it writes its keys:
-// clears the digit histograms of all passes and gathers the AND / OR of the
-// keys (topk_note per key, topk_publish once per thread before the barrier
-// that makes the keys visible).
-__device__ __forceinline__ void topk_clear(EpiSmem &sm) {
-  int *h = &sm.hist[0][0][0];
-  for (int i = 4 * threadIdx.x; i < 4 * kWaves * 256; i += 4 * kThreads)
-    *reinterpret_cast<u32x4 *>(&h[i]) = u32x4{0u, 0u, 0u, 0u};
+template <int D>
+union KernelSmem {
+  SplitSmem<D> split;
+  EpiSmem epi;
+};
+
+// LDS written by some lanes of a wavefront and read by others: wait for the
+// wavefront's LDS operations, and keep the compiler from moving accesses
+// across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
 }
-__device__ __forceinline__ void topk_publish(EpiSmem &sm, uint32_t kor, uint32_t kand) {
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kDppQuad1032>(~0u, v));
+  v = min(v, dpp_u32<kDppQuad2301>(~0u, v));
+  v = min(v, dpp_u32<kDppRowHalfMirror>(~0u, v));
+  v = min(v, dpp_u32<kDppRowMirror>(~0u, v));
+  v = min(v, dpp_u32<kDppRowBcast15, 0xa>(~0u, v));
+  v = min(v, dpp_u32<kDppRowBcast31, 0xc>(~0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Radix select over the keys, run by one wavefront: the threshold over 4 x 8
+// bits, most significant digit first (digits shared by every key skipped,
+// the passes stop once the chosen digit's bucket is taken whole), then the
+// keys above it and the equal ones in id order until k_eff.  Writes the
+// selected ids ascending to out[0..keff).
+__device__ __forceinline__ void wave_radix_select(const uint32_t *keys, int N, int keff,
+                                                  int32_t *out, SelectSmem &ss) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+  for (int n = lane; n < N; n += 64) {
+    const uint32_t key = keys[n];
+    kor |= key;
+    kand &= key;
+  }
   kor = wave_or(kor);
   kand = wave_and(kand);
-  if ((threadIdx.x & 63) == 0) {
-    sm.kor[threadIdx.x >> 6] = kor;
-    sm.kand[threadIdx.x >> 6] = kand;
-  }
-}
-
-// Selects the k_eff = min(k, N) largest keys[0..N) (unsigned compare), equal
-// keys going to the lower index, and writes their indices in ascending order
-// to out[0..k_eff), -1 after.  Called by every thread of the workgroup after
-// topk_clear / topk_publish and a barrier that made the keys visible.
-//   threshold  radix select over 4 x 8 bits, most significant digit first;
-//              digits shared by every key are skipped, and the passes stop
-//              once the chosen digit's bucket is taken whole.  Each wavefront
-//              counts the digits of its keys into a private 256-bin
-//              histogram of the pass (cleared beforehand, so one barrier per
-//              pass suffices); every wavefront then sums the eight histograms
-//              and finds the same digit on its own.
-//   compaction each wavefront owns a contiguous segment of the keys and takes
-//              those whose decided bits are above the threshold, and those
-//              equal to it in index order until k_eff; ballots give positions
-//              inside a row of 64, per-wavefront counts the offset of each
-//              segment.
-__device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int32_t *out) {
-  const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
-  const int keff = k < N ? k : N;
-  if (keff == N) {  // every block is selected (also N == 0)
-    for (int r = threadIdx.x; r < k; r += kThreads) out[r] = r < N ? r : -1;
-    return;
-  }
-  uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) {
-    kor |= sm.kor[v];
-    kand &= sm.kand[v];
-  }
   const uint32_t common = ~(kor ^ kand);
-
   uint32_t prefix = 0u, mask = 0u;
   int remaining = keff;
   for (int pass = 0; pass < 4; ++pass) {
@@ -299,23 +353,17 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
       mask |= dmask;
       continue;
     }
-    int(*hist)[256] = sm.hist[pass];
-    for (int n = threadIdx.x; n < N; n += kThreads) {
-      const uint32_t kv = sm.keys[n];
-      if ((kv & mask) == prefix) atomicAdd(&hist[w][(kv >> shift) & 255u], 1);
+    *reinterpret_cast<u32x4 *>(&ss.hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+    wave_lds_sync();
+    for (int n = lane; n < N; n += 64) {
+      const uint32_t key = keys[n];
+      if ((key & mask) == prefix) atomicAdd(&ss.hist[(key >> shift) & 255u], 1);
     }
-    __syncthreads();
-    // lane l sums bins 255-4l .. 252-4l (descending) over the wavefronts and
-    // finds the bin where the count of keys from the top reaches `remaining`
-    int c[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const u32x4 hv = *reinterpret_cast<const u32x4 *>(&hist[v][252 - 4 * lane]);
-      c[0] += (int)hv[3];
-      c[1] += (int)hv[2];
-      c[2] += (int)hv[1];
-      c[3] += (int)hv[0];
-    }
+    wave_lds_sync();
+    // lane l holds bins 255-4l .. 252-4l (descending) and finds the bin where
+    // the count of keys from the top reaches `remaining`
+    const u32x4 hv = *reinterpret_cast<const u32x4 *>(&ss.hist[252 - 4 * lane]);
+    const int c[4] = {(int)hv[3], (int)hv[2], (int)hv[1], (int)hv[0]};
     const int tot = c[0] + c[1] + c[2] + c[3];
     int above = wave_inclusive_scan(tot) - tot;
     int digit = -1, rem = 0, cnt = 0;
@@ -332,40 +380,17 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
     prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, leader) << shift;
     mask |= dmask;
     remaining = __builtin_amdgcn_readlane(rem, leader);
+    wave_lds_sync();  // every lane has read the histogram before the next pass clears it
     if (remaining == __builtin_amdgcn_readlane(cnt, leader)) break;  // bucket taken whole
   }
   const uint32_t thr = prefix;
   const int need_eq = remaining;
-
-  // segment of wavefront w: rows of 64 keys [w*seg, min(N, (w+1)*seg))
-  const int seg = ((N + kWaves - 1) / kWaves + 63) / 64 * 64;
-  const int n0 = w * seg, n1 = min(N, n0 + seg);
-  int gt = 0, eq = 0;
-  for (int base = n0; base < n1; base += 64) {
-    const int n = base + lane;
-    const uint32_t kv = n < n1 ? sm.keys[n] & mask : 0u;
-    gt += __builtin_popcountll(__ballot(n < n1 && kv > thr));
-    eq += __builtin_popcountll(__ballot(n < n1 && kv == thr));
-  }
-  if (lane == 0) {
-    sm.seg_gt[w] = gt;
-    sm.seg_eq[w] = eq;
-  }
-  __syncthreads();
   int taken = 0, eq_before = 0;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) {
-    if (v < w) {
-      const int e = sm.seg_eq[v];
-      taken += sm.seg_gt[v] + min(e, max(0, need_eq - eq_before));
-      eq_before += e;
-    }
-  }
-  for (int base = n0; base < n1; base += 64) {
+  for (int base = 0; base < N; base += 64) {
     const int n = base + lane;
-    const uint32_t kv = n < n1 ? sm.keys[n] & mask : 0u;
-    const bool is_gt = n < n1 && kv > thr;
-    const bool is_eq = n < n1 && kv == thr;
+    const uint32_t kv = n < N ? keys[n] & mask : 0u;
+    const bool is_gt = n < N && kv > thr;
+    const bool is_eq = n < N && kv == thr;
     const uint64_t eqm = __ballot(is_eq);
     const bool sel = is_gt || (is_eq && eq_before + lanes_below(eqm) < need_eq);
     const uint64_t selm = __ballot(sel);
@@ -373,16 +398,192 @@ __device__ __forceinline__ void select_topk_block(EpiSmem &sm, int N, int k, int
     taken += __builtin_popcountll(selm);
     eq_before += __builtin_popcountll(eqm);
   }
-  for (int r = keff + threadIdx.x; r < k; r += kThreads) out[r] = -1;
 }
 
-template <int D>
-union KernelSmem {
-  SplitSmem<D> split;
-  EpiSmem epi;
-};
+// k-th largest (kk >= 1) of the values v[i] of every lane (0 stands for
+// none): the largest t with #{v >= t} >= kk, decided bit by bit from the top
+// with ballots.
+template <int NV>
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&v)[NV], int kk) {
+  uint32_t any = 0u;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) any |= v[i];
+  any = wave_or(any);
+  uint32_t t = 0u;
+  for (int bit = any ? 31 - __builtin_clz(any) : -1; bit >= 0; --bit) {
+    const uint32_t trial = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cnt += __builtin_popcountll(__ballot(v[i] >= trial));
+    if (cnt >= kk) t = trial;
+  }
+  return t;
+}
+
+// Lower bound t0 of the k-th largest key (k <= 64).  Key n sits in lane
+// n % 64; the lanes are cut into R groups of S (R = 2k rounded up to a
+// power of two, at most 64), and t0 is the k-th largest of the R group
+// maxima: the largest key of at least k distinct groups, so at least k keys
+// are >= t0.  The k-th largest is found by counting, for each group maximum,
+// the maxima above it and those not below it (readlane broadcasts, every
+// comparison independent of the others).
+__device__ __forceinline__ uint32_t topk_filter(const uint32_t *keys, int N, int k) {
+  const int lane = threadIdx.x & 63;
+  int R = 2;
+  while (R < 2 * k && R < 64) R <<= 1;
+  const int S = 64 / R;
+  // this lane's largest key: four independent LDS reads per step
+  uint32_t gm = 0u;
+  for (int base = 0; base < N; base += 256) {
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = base + 64 * u + lane;
+      v[u] = n < N ? keys[n] : 0u;
+    }
+    gm = max(gm, max(max(v[0], v[1]), max(v[2], v[3])));
+  }
+  if (S >= 2) gm = max(gm, dpp_u32<kDppQuad1032>(0u, gm));
+  if (S >= 4) gm = max(gm, dpp_u32<kDppQuad2301>(0u, gm));
+  if (S >= 8) gm = max(gm, dpp_u32<kDppRowHalfMirror>(0u, gm));
+  if (S >= 16) gm = max(gm, dpp_u32<kDppRowMirror>(0u, gm));
+  if (S >= 32) gm = max(gm, (uint32_t)__shfl_xor((int)gm, 16));
+  if (S >= 64) gm = max(gm, (uint32_t)__shfl_xor((int)gm, 32));
+  // every lane of a group holds its maximum; group r's sits at lane r * S.
+  // Four groups per step, each with its own counters (independent chains).
+  int above[4] = {0, 0, 0, 0}, not_below[4] = {0, 0, 0, 0};
+  for (int r0 = 0; r0 < R; r0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = r0 + u < R ? r0 + u : r0;  // R is a power of two >= 2
+      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)gm, r * S);
+      const bool in = r0 + u < R;
+      above[u] += (in && v > gm) ? 1 : 0;
+      not_below[u] += (in && v >= gm) ? 1 : 0;
+    }
+  }
+  const int ab = above[0] + above[1] + above[2] + above[3];
+  const int nb = not_below[0] + not_below[1] + not_below[2] + not_below[3];
+  const uint64_t hit = __ballot(ab < k && k <= nb);
+  return (uint32_t)__builtin_amdgcn_readlane((int)gm, __builtin_ctzll(hit));
+}
+
+// Selection among C <= 64 candidates, candidate p in lane p, in ascending
+// block id: a candidate's rank is the number of candidates with a larger
+// key or an equal key and a lower id (readlane broadcasts, independent
+// comparisons); the keff of rank < keff are written in id order.
+__device__ __forceinline__ void select_candidates_rank(const SelectSmem &ss, int C, int keff,
+                                                       int32_t *out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t ck = lane < C ? ss.cand_key[lane] : 0u;
+  const int32_t ci = lane < C ? ss.cand_id[lane] : -1;
+  // four candidates per step, each with its own counter (independent chains)
+  int rank[4] = {0, 0, 0, 0};
+  for (int m0 = 0; m0 < C; m0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int m = m0 + u;
+      const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)ck, m < C ? m : m0);
+      rank[u] += (m < C && (km > ck || (km == ck && m < lane))) ? 1 : 0;
+    }
+  }
+  const bool sel = lane < C && rank[0] + rank[1] + rank[2] + rank[3] < keff;
+  const uint64_t selm = __ballot(sel);
+  if (sel) out[lanes_below(selm)] = ci;
+}
+
+// Selection among the C (<= 64 * NV) candidates in ss, slot p = candidate p
+// in ascending block id: the keff largest keys, ties to the lower slot,
+// written in slot order to out[0..keff).
+template <int NV>
+__device__ __forceinline__ void select_candidates(const SelectSmem &ss, int C, int keff, int32_t *out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t ck[NV];
+  int32_t ci[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int p = lane + 64 * i;
+    ck[i] = p < C ? ss.cand_key[p] : 0u;
+    ci[i] = p < C ? ss.cand_id[p] : -1;
+  }
+  const uint32_t thr = wave_kth_largest<NV>(ck, keff);
+  int ngt = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) ngt += __builtin_popcountll(__ballot(lane + 64 * i < C && ck[i] > thr));
+  const int need_eq = keff - ngt;
+  int taken = 0, eq_before = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bool valid = lane + 64 * i < C;
+    const bool is_gt = valid && ck[i] > thr;
+    const bool is_eq = valid && ck[i] == thr;
+    const uint64_t eqm = __ballot(is_eq);
+    const bool sel = is_gt || (is_eq && eq_before + lanes_below(eqm) < need_eq);
+    const uint64_t selm = __ballot(sel);
+    if (sel) out[taken + lanes_below(selm)] = ci[i];
+    taken += __builtin_popcountll(selm);
+    eq_before += __builtin_popcountll(eqm);
+  }
+}
+
+// Top-k selection run by one whole wavefront: the k_eff = min(k, N) largest
+// keys[0..N) (unsigned compare, equal keys going to the lower index), their
+// indices written in ascending order to out[0..k_eff) and -1 after, up to k.
+//
+// A filter bound t0 (topk_filter) leaves the keys >= t0 as candidates,
+// usually a few more than k; they are compacted in id order and ranked
+// against each other (up to 64 of them), or the exact k-th largest among
+// them is found by ballot bisection (up to kMaxCandidates).  More
+// candidates, or k > 64, fall back to the radix select.
+// Either way the result is the exact top k under the tie rule.
+constexpr int kMaxCandidates = 256;
+__device__ __forceinline__ void wave_select_topk(const uint32_t *keys, int N, int k, int32_t *out,
+                                                 SelectSmem &ss) {
+  const int lane = threadIdx.x & 63;
+  const int keff = k < N ? k : N;
+  if (keff == N) {  // every block is selected (also N == 0)
+    for (int r = lane; r < k; r += 64) out[r] = r < N ? r : -1;
+    return;
+  }
+  bool done = false;
+  if (k <= 64) {
+    const uint32_t t0 = topk_filter(keys, N, k);
+    int C = 0;
+    for (int base = 0; base < N; base += 256) {
+      uint32_t key[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int n = base + 64 * u + lane;
+        key[u] = n < N ? keys[n] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int n = base + 64 * u + lane;
+        const bool cand = n < N && key[u] >= t0;
+        const uint64_t bm = __ballot(cand);
+        const int pos = C + lanes_below(bm);
+        if (cand && pos < kMaxCandidates) {
+          ss.cand_key[pos] = key[u];
+          ss.cand_id[pos] = n;
+        }
+        C += __builtin_popcountll(bm);
+      }
+    }
+    if (C <= kMaxCandidates) {
+      wave_lds_sync();
+      if (C <= 64)
+        select_candidates_rank(ss, C, keff, out);
+      else
+        select_candidates<kMaxCandidates / 64>(ss, C, keff, out);
+      done = true;
+    }
+  }
+  if (!done) wave_radix_select(keys, N, keff, out, ss);
+  for (int r = keff + lane; r < k; r += 64) out[r] = -1;
+}
 
 // Outputs of a (b, g) with no chunk to attend (empty context).
+template <int kMode>
 __device__ __forceinline__ void write_empty(const AttnArgs &a, int b, int g, int D) {
   const int G = a.group;
   for (int i = threadIdx.x; i < G * D; i += kThreads)
@@ -390,17 +591,21 @@ __device__ __forceinline__ void write_empty(const AttnArgs &a, int b, int g, int
   if (a.lse != nullptr)
     for (int h = threadIdx.x; h < G; h += kThreads)
       a.lse[(int64_t)b * a.num_q_heads + g * G + h] = kNegInf;
-  if (a.score_out != nullptr)
-    for (int n = threadIdx.x; n < a.max_blocks; n += kThreads)
-      a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = 0.f;
-  if (a.idx_out != nullptr)
-    for (int r = threadIdx.x; r < a.k; r += kThreads)
-      a.idx_out[((int64_t)b * a.num_kv_heads + g) * a.k + r] = -1;
-  if (a.sel_log != nullptr)
-    for (int r = threadIdx.x; r < a.k; r += kThreads) {
-      const int64_t i = ((int64_t)b * a.num_kv_heads + g) * a.k + r;
-      a.sel_log[i] = a.sel[i];
-    }
+  if constexpr (kMode == kModeScored) {
+    if (a.score_out != nullptr)
+      for (int n = threadIdx.x; n < a.max_blocks; n += kThreads)
+        a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = 0.f;
+    if (a.idx_out != nullptr)
+      for (int r = threadIdx.x; r < a.k; r += kThreads)
+        a.idx_out[((int64_t)b * a.num_kv_heads + g) * a.k + r] = -1;
+  }
+  if constexpr (mode_sparse(kMode)) {
+    if (a.sel_log != nullptr)
+      for (int r = threadIdx.x; r < a.k; r += kThreads) {
+        const int64_t i = ((int64_t)b * a.num_kv_heads + g) * a.k + r;
+        a.sel_log[i] = a.sel[i];
+      }
+  }
 }
 
 // Two-level merge, run by the last workgroup of group q to arrive: the
@@ -448,15 +653,19 @@ __device__ __forceinline__ void merge_group(const AttnArgs &a, int b, int g, int
   }
 }
 
-// Writes the workgroup partial from the eight wavefront states (and, in full
-// mode with scores, the block masses rescaled to the partial's max), then
-// counts the workgroup's arrival.  Returns true in the last of the nact
-// workgroups of (b, g), which then runs the epilogue.  Two-level: the
-// arrival is first counted in the split's group; the group's last arrival
-// merges the group and counts it among the groups of (b, g).
-template <int D, bool kTwoLevel = false>
-__device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact, int c_begin,
-                             int c_end, int T, SplitSmem<D> &sm, int *last_flag) {
+
+// Hand-off of the workgroup partial (the eight wavefront states merged, and
+// in scored mode the block masses rescaled to the partial's max) to the
+// epilogue.  Every workgroup stores its partial with coherent device-scope
+// stores and waits for them to complete before its arrival is counted, so
+// the last arrival of (b, g) -- which returns true and runs the epilogue --
+// finds every partial in memory.  Two levels: the arrival is first counted
+// in the split's group; the group's last arrival merges the group and
+// counts it among the groups of (b, g).
+template <int D, int kMode, bool kTwoLevel>
+__device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, int s, int nact,
+                                             int c_begin, int c_end, int T, SplitSmem<D> &sm,
+                                             int *last_flag) {
   const int G = a.group;
   const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
   const __amdgpu_buffer_rsrc_t po = buffer(a.part_o + head0 * a.nsplit * D,
@@ -483,7 +692,7 @@ __device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, in
       store_agent(a.part_ml + row * 2 + 1, l);
     }
   }
-  if (a.stats != nullptr) {
+  if constexpr (kMode == kModeScored) {
     const int nb0 = c_begin / kChunksPerBlock;
     const int nblk = (c_end - c_begin + kChunksPerBlock - 1) / kChunksPerBlock;
     const int N = (T + kBlockTokens - 1) / kBlockTokens;
@@ -518,7 +727,7 @@ __device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, in
     }
     __syncthreads();
     const bool group_last = *last_flag != 0;
-    __syncthreads();
+    __syncthreads();  // every thread has read the flag before it is written again
     if (!group_last) return false;
     merge_group<D>(a, b, g, q, gsize);
     __builtin_amdgcn_s_waitcnt(0);
@@ -533,273 +742,342 @@ __device__ __forceinline__ bool finish_split(const AttnArgs &a, int b, int g, in
     *last_flag = last ? 1 : 0;
   }
   __syncthreads();
-  const bool last = *last_flag != 0;
-  __syncthreads();  // the epilogue reuses the LDS of the split pass
-  return last;
+  // the split LDS is no longer read: the epilogue may overwrite it at once
+  return *last_flag != 0;
 }
 
-// Merges the nact split partials of (b, g) into out / lse; in full mode with
-// block masses also the block scores and the top-k.  Runs in the last
-// workgroup of (b, g) to finish its split pass.
-//
-// out: thread -> (head h, 4 columns c) item and a stripe of the splits.  The
-// loads that do not depend on each other are issued up front, in the order
-// they are needed: the (max, sum) partials, the first batch of partial
-// outputs, the block masses of block threadIdx.x.  They are straight-line
-// code (a branch around a load makes the compiler wait for the load at the
-// join), sized by the template arguments so that few are wasted: kBatch
-// split partials per thread, masses of GP >= G heads.  Loads needed only by
-// larger shapes (a second head per wavefront, more than 64 splits, blocks
-// past kThreads) sit behind branches.  A lane out of range reads at an
-// offset past the resource, which gives 0 without touching memory.
-template <int D, int kBatch, int GP, bool kTwoLevel = false>
-__device__ __forceinline__ void epilogue_impl(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
-  const int G = a.group;
-  const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
-  const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
-  const int items = G * (D / 4);  // <= kThreads
-  const int stripes = kThreads / items;
-  const int item = threadIdx.x % items, stripe = threadIdx.x / items;
-  const bool active = stripe < stripes;
-  const int h_item = item / (D / 4), c_item = 4 * (item % (D / 4));
-  // the partials the output merge reads: the splits', or with two levels the
-  // groups'
-  const int nparts = kTwoLevel ? (nact + kGroupSplits - 1) / kGroupSplits : nact;
-  const int pstride = kTwoLevel ? kMaxGroups : a.nsplit;
-  const __amdgpu_buffer_rsrc_t po =
-      kTwoLevel ? buffer(a.part_o2 + head0 * kMaxGroups * D, (uint32_t)(G * kMaxGroups * D * 4))
-                : buffer(a.part_o + head0 * a.nsplit * D, (uint32_t)(G * a.nsplit * D * 4));
-  // loads of partials stripe + stripes * (j0 + j)
-  auto load_batch = [&](f32x4 (&v)[kBatch], int j0) {
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int s = stripe + stripes * (j0 + j);
-      const uint32_t off = (active && s < nparts)
-                               ? (uint32_t)(((h_item * pstride + s) * D + c_item) * 4)
-                               : 0x80000000u;
-      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(po, off, 0, kCoherent));
-    }
-  };
-  const int N = (T + kBlockTokens - 1) / kBlockTokens;
-  // (max, sum) of the splits of heads w and w + kWaves (one wavefront a head)
-  const __amdgpu_buffer_rsrc_t pml = buffer(a.part_ml + head0 * a.nsplit * 2,
-                                            (uint32_t)(G * a.nsplit * 2 * 4));
-  auto load_ml = [&](int hh, int j, float &m, float &l) {
+// Loads and reductions of the per-head statistics of the split partials.
+// Wavefront w serves heads w and w + kWaves; lane j of it split j (and
+// j + 64, ...).  Every load is issued before the first use; loads a shape
+// does not need read past their buffer resource, which returns 0 without a
+// memory access.
+template <int HH, bool kTwoLevel>
+struct HeadStats {
+  float ms[HH][kMaxSplits / 64], ls[HH][kMaxSplits / 64];
+  float m2[HH];
+
+  __device__ __forceinline__ void load_ml(const AttnArgs &a, int64_t head0, int nact, int hh,
+                                          int j) {
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
     const int h = w + kWaves * hh, s = lane + 64 * j;
-    const bool in = h < G && s < nact;
+    const bool in = h < a.group && s < nact;
+    const __amdgpu_buffer_rsrc_t pml = buffer(a.part_ml + head0 * a.nsplit * 2,
+                                              (uint32_t)(a.group * a.nsplit * 2 * 4));
     // two 32-bit loads: this toolchain compiles the 64-bit raw buffer load
     // builtin into a single 32-bit load whose word fills both halves
     const uint32_t off = in ? (uint32_t)((h * a.nsplit + s) * 2 * 4) : 0x80000000u;
     const uint32_t m_bits = __builtin_amdgcn_raw_buffer_load_b32(pml, off, 0, kCoherent);
     const uint32_t l_bits = __builtin_amdgcn_raw_buffer_load_b32(pml, off + 4u, 0, kCoherent);
-    m = in ? __builtin_bit_cast(float, m_bits) : kNegInf;
-    l = in ? __builtin_bit_cast(float, l_bits) : 0.f;
-  };
-  constexpr int HH = GP > kWaves ? 2 : 1;  // heads per wavefront
-  float ms[HH][kMaxSplits / 64], ls[HH][kMaxSplits / 64];
-  load_ml(0, 0, ms[0][0], ls[0][0]);
-  f32x4 first[kBatch];
-  load_batch(first, 0);
-  // two levels: the group maxima of heads w and w + kWaves (lane q: group q)
-  float m2[HH];
-  if constexpr (kTwoLevel) {
-    const __amdgpu_buffer_rsrc_t pml2 =
-        buffer(a.part_ml2 + head0 * kMaxGroups * 2, (uint32_t)(G * kMaxGroups * 2 * 4));
+    ms[hh][j] = in ? __builtin_bit_cast(float, m_bits) : kNegInf;
+    ls[hh][j] = in ? __builtin_bit_cast(float, l_bits) : 0.f;
+  }
+
+  // The loads every shape needs: splits 0..63 of head w (and the group
+  // maxima with two levels), straight-line.
+  __device__ __forceinline__ void load_first(const AttnArgs &a, int64_t head0, int nact, int nparts) {
+    const int G = a.group;
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
+    load_ml(a, head0, nact, 0, 0);
+    if constexpr (kTwoLevel) {
+      const __amdgpu_buffer_rsrc_t pml2 =
+          buffer(a.part_ml2 + head0 * kMaxGroups * 2, (uint32_t)(G * kMaxGroups * 2 * 4));
+#pragma unroll
+      for (int hh = 0; hh < HH; ++hh) {
+        const int h = w + kWaves * hh;
+        const bool in = h < G && lane < nparts;
+        const uint32_t off = in ? (uint32_t)((h * kMaxGroups + lane) * 2 * 4) : 0x80000000u;
+        const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(pml2, off, 0, kCoherent);
+        m2[hh] = in ? __builtin_bit_cast(float, bits) : kNegInf;
+      }
+    }
+  }
+
+  // The loads of larger shapes (a second head per wavefront, more than 64
+  // splits), behind uniform branches: issued after every straight-line load,
+  // since a branch around a load makes the compiler wait for it at the join.
+  __device__ __forceinline__ void load_rest(const AttnArgs &a, int64_t head0, int nact) {
+    const int w = uniform(threadIdx.x >> 6);
+#pragma unroll
+    for (int hh = 0; hh < HH; ++hh)
+#pragma unroll
+      for (int j = 0; j < kMaxSplits / 64; ++j) {
+        if (hh == 0 && j == 0) continue;
+        ms[hh][j] = kNegInf;
+        ls[hh][j] = 0.f;
+        if (w + kWaves * hh < a.group && 64 * j < nact) load_ml(a, head0, nact, hh, j);
+      }
+  }
+
+  // Global max M and sum L of each head and the per-split (two levels: per
+  // group) rescale factors, into LDS.
+  __device__ __forceinline__ void reduce(const AttnArgs &a, int nact, int nparts, EpiSmem &sm) {
+    const int G = a.group;
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
 #pragma unroll
     for (int hh = 0; hh < HH; ++hh) {
       const int h = w + kWaves * hh;
-      const bool in = h < G && lane < nparts;
-      const uint32_t off = in ? (uint32_t)((h * kMaxGroups + lane) * 2 * 4) : 0x80000000u;
-      const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(pml2, off, 0, kCoherent);
-      m2[hh] = in ? __builtin_bit_cast(float, bits) : kNegInf;
-    }
-  }
-  // block masses (stored relative to their split's max) of block threadIdx.x
-  const __amdgpu_buffer_rsrc_t pst =
-      buffer(a.stats != nullptr ? a.stats + head0 * a.max_blocks : nullptr,
-             a.stats != nullptr ? (uint32_t)(G * a.max_blocks * 4) : 0u);
-  float mass_pre[GP];
+      if (h >= G) continue;
+      float mx = kNegInf;
 #pragma unroll
-  for (int h = 0; h < GP; ++h) {
-    const int n = threadIdx.x;
-    const uint32_t off = (h < G && n < N) ? (uint32_t)((h * a.max_blocks + n) * 4) : 0x80000000u;
-    mass_pre[h] =
-        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pst, off, 0, kCoherent));
-  }
-  // masses of block threadIdx.x + kThreads (more than kThreads blocks)
-  float mass_pre1[GP];
+      for (int j = 0; j < kMaxSplits / 64; ++j) mx = fmaxf(mx, ms[hh][j]);
+      const float M = wave_max(mx);
+      float lsum = 0.f;
 #pragma unroll
-  for (int h = 0; h < GP; ++h) mass_pre1[h] = 0.f;
-  if (a.stats != nullptr && N > kThreads) {
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-      const int n = threadIdx.x + kThreads;
-      const uint32_t off =
-          (h < G && n < N) ? (uint32_t)((h * a.max_blocks + n) * 4) : 0x80000000u;
-      mass_pre1[h] =
-          __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pst, off, 0, kCoherent));
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < HH; ++hh)
-#pragma unroll
-    for (int j = 0; j < kMaxSplits / 64; ++j) {
-      if (hh == 0 && j == 0) continue;
-      ms[hh][j] = kNegInf;
-      ls[hh][j] = 0.f;
-      if (w + kWaves * hh < G && 64 * j < nact) load_ml(hh, j, ms[hh][j], ls[hh][j]);
-    }
-
-  // the top-k histograms are cleared while the loads are in flight
-  if (a.idx_out != nullptr) topk_clear(sm);
-
-  // per head: global max / sum and the per-split rescale factors
-#pragma unroll
-  for (int hh = 0; hh < HH; ++hh) {
-    const int h = w + kWaves * hh;
-    if (h >= G) continue;
-    float mx = kNegInf;
-#pragma unroll
-    for (int j = 0; j < kMaxSplits / 64; ++j) mx = fmaxf(mx, ms[hh][j]);
-    const float M = wave_max(mx);
-    float lsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxSplits / 64; ++j) {
-      const int s = lane + 64 * j;
-      const float f = rescale(ms[hh][j], M);
-      if (s < nact) sm.f[h][s] = f;
-      lsum += f * ls[hh][j];
-    }
-    if constexpr (kTwoLevel) {
-      if (lane < nparts) sm.f2[h][lane] = rescale(m2[hh], M);
-    }
-    const float L = wave_sum(lsum);
-    if (lane == 0) {
-      sm.M[h] = M;
-      sm.L[h] = L;
-      sm.invL[h] = L > 0.f ? 1.f / L : 0.f;
-    }
-  }
-  __syncthreads();
-
-  f32x4 out_v = {0.f, 0.f, 0.f, 0.f};
-  {
-    const int per_stripe = (nparts - stripe + stripes - 1) / stripes;  // partials of this stripe
-    auto factor = [&](int s) {
-      if constexpr (kTwoLevel)
-        return sm.f2[h_item][s];
-      else
-        return sm.f[h_item][s];
-    };
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int s = stripe + stripes * j;
-      if (active && s < nparts) acc += factor(s) * first[j];
-    }
-    for (int j0 = kBatch; j0 < per_stripe; j0 += kBatch) {
-      f32x4 v[kBatch];
-      load_batch(v, j0);
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int s = stripe + stripes * (j0 + j);
-        if (active && s < nparts) acc += factor(s) * v[j];
+      for (int j = 0; j < kMaxSplits / 64; ++j) {
+        const int s = lane + 64 * j;
+        const float f = rescale(ms[hh][j], M);
+        if (s < nact) sm.f[h][s] = f;
+        lsum += f * ls[hh][j];
+      }
+      if constexpr (kTwoLevel) {
+        if (lane < nparts) sm.f2[h][lane] = rescale(m2[hh], M);
+      }
+      const float L = wave_sum(lsum);
+      if (lane == 0) {
+        sm.M[h] = M;
+        sm.L[h] = L;
+        sm.invL[h] = L > 0.f ? 1.f / L : 0.f;
       }
     }
-    if (stripes > 1) {
-      sm.red[threadIdx.x] = acc;
-      __syncthreads();
-      if (threadIdx.x < items)
-        for (int st = 1; st < stripes; ++st) acc += sm.red[st * items + threadIdx.x];
-    }
-    out_v = acc;
   }
-  // every global store of the epilogue comes after its last barrier, so no
-  // barrier waits for stores to complete
-  auto store_outputs = [&]() {
-    if ((int)threadIdx.x < items) {
-      const float L = sm.L[h_item];
-      const f32x4 o = L > 0.f ? out_v * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4 *>(a.out + (head0 + h_item) * D + c_item) = o;
+};
+
+// Output merge of the partials of (b, g) into out / lse by the nw
+// wavefronts [w0, w0 + nw) of the workgroup.  An item is (head h, 4
+// columns); each of those wavefronts serves iw items (16, 32 or 64) with
+// 64 / iw stripes of the partials per item, and the stripes are summed with
+// lane shuffles, so the merge needs no barrier.  Items beyond nw * iw come
+// in further passes.  The first batch of loads of the first pass is issued
+// early (issue_first), before the per-head factors are known.
+template <int D, int kBatch, bool kTwoLevel>
+struct OutputMerge {
+  __amdgpu_buffer_rsrc_t po;
+  int items, iw, stripes, span, nparts, pstride, il, stripe, ow;
+  f32x4 first[kBatch];
+
+  __device__ __forceinline__ void init(const AttnArgs &a, int64_t head0, int nact, int ow_, int nw) {
+    const int G = a.group;
+    items = G * (D / 4);
+    const int per_wave = (items + nw - 1) / nw;
+    iw = per_wave > 32 ? 64 : per_wave > 16 ? 32 : 16;
+    stripes = 64 / iw;
+    span = nw * iw;
+    const int lane = threadIdx.x & 63;
+    il = lane & (iw - 1);
+    stripe = lane / iw;
+    ow = ow_;
+    nparts = kTwoLevel ? (nact + kGroupSplits - 1) / kGroupSplits : nact;
+    pstride = kTwoLevel ? kMaxGroups : a.nsplit;
+    po = kTwoLevel ? buffer(a.part_o2 + head0 * kMaxGroups * D, (uint32_t)(G * kMaxGroups * D * 4))
+                   : buffer(a.part_o + head0 * a.nsplit * D, (uint32_t)(G * a.nsplit * D * 4));
+  }
+  __device__ __forceinline__ int item(int pass) const { return pass * span + ow * iw + il; }
+  // loads of partials stripe + stripes * (j0 + j), j < kBatch, of item `it`
+  // (an item past the end reads nothing)
+  __device__ __forceinline__ void issue(f32x4 (&v)[kBatch], int it, int j0) const {
+    const int h = it / (D / 4), c = 4 * (it % (D / 4));
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int s = stripe + stripes * (j0 + j);
+      const uint32_t off = (it < items && s < nparts)
+                               ? (uint32_t)(((h * pstride + s) * D + c) * 4)
+                               : 0x80000000u;
+      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(po, off, 0, kCoherent));
     }
-    if (a.lse != nullptr && threadIdx.x < G) {
-      const float L = sm.L[threadIdx.x];
-      a.lse[head0 + threadIdx.x] = L > 0.f ? (sm.M[threadIdx.x] + __log2f(L)) * kLn2 : kNegInf;
+  }
+  __device__ __forceinline__ void issue_first(bool participate) {
+    issue(first, participate ? item(0) : items, 0);
+  }
+  __device__ __forceinline__ void accumulate(f32x4 &acc, const f32x4 (&v)[kBatch], int it, int j0,
+                                             const EpiSmem &sm) const {
+    const int h = it / (D / 4);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int s = stripe + stripes * (j0 + j);
+      if (it < items && s < nparts) acc += (kTwoLevel ? sm.f2[h][s] : sm.f[h][s]) * v[j];
     }
+  }
+  // Runs every pass and writes out (and lse from the first wavefront).
+  __device__ __forceinline__ void run(const AttnArgs &a, int64_t head0, const EpiSmem &sm) {
+    const int lane = threadIdx.x & 63;
+    const int per_stripe = (nparts + stripes - 1) / stripes;
+    for (int pass = 0; pass * span < items; ++pass) {
+      const int it = item(pass);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (pass == 0) accumulate(acc, first, it, 0, sm);
+      for (int j0 = pass == 0 ? kBatch : 0; j0 < per_stripe; j0 += kBatch) {
+        f32x4 v[kBatch];
+        issue(v, it, j0);
+        accumulate(acc, v, it, j0, sm);
+      }
+      for (int off = iw; off < 64; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off);
+        acc.y += __shfl_xor(acc.y, off);
+        acc.z += __shfl_xor(acc.z, off);
+        acc.w += __shfl_xor(acc.w, off);
+      }
+      if (stripe == 0 && it < items) {
+        const int h = it / (D / 4), c = 4 * (it % (D / 4));
+        const float L = sm.L[h];
+        const f32x4 o = L > 0.f ? acc * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4 *>(a.out + (head0 + h) * D + c) = o;
+      }
+    }
+    if (a.lse != nullptr && ow == 0 && lane < a.group) {
+      const float L = sm.L[lane];
+      a.lse[head0 + lane] = L > 0.f ? (sm.M[lane] + __log2f(L)) * kLn2 : kNegInf;
+    }
+  }
+};
+
+// Epilogue of the full and sparse modes: every wavefront merges output.
+template <int D, int kBatch, int HH, bool kTwoLevel, int kMode>
+__device__ __forceinline__ void epilogue_plain(const AttnArgs &a, int b, int g, int nact, EpiSmem &sm) {
+  const int w = uniform(threadIdx.x >> 6);
+  const int64_t head0 = (int64_t)b * a.num_q_heads + g * a.group;
+  OutputMerge<D, kBatch, kTwoLevel> mg;
+  mg.init(a, head0, nact, w, kWaves);
+  HeadStats<HH, kTwoLevel> hs;
+  hs.load_first(a, head0, nact, mg.nparts);
+  mg.issue_first(true);
+  hs.load_rest(a, head0, nact);
+  hs.reduce(a, nact, mg.nparts, sm);
+  __syncthreads();
+  mg.run(a, head0, sm);
+  if constexpr (mode_sparse(kMode)) {
     if (a.sel_log != nullptr) {
       const int64_t r0 = ((int64_t)b * a.num_kv_heads + g) * a.k;
       for (int r = threadIdx.x; r < a.k; r += kThreads) a.sel_log[r0 + r] = a.sel[r0 + r];
     }
-  };
-  if (a.stats == nullptr) {
-    store_outputs();
-    return;
   }
-
-  // block score: sum over the group's heads of the softmax mass of the block
-  // (mass stored relative to its split's max; f brings it to the head's max)
-  const int blocks_per_split = a.chunks_per_wg / kChunksPerBlock;
-  float score0 = 0.f;  // score of block n = thread, stored after the barrier
-  uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-  for (int n = threadIdx.x; n < a.max_blocks; n += kThreads) {
-    float score = 0.f;
-    if (n < N) {
-      const int s = n / blocks_per_split;
-#pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        if (h >= G) continue;
-        const float mass = n < kThreads       ? mass_pre[h]
-                           : n < 2 * kThreads ? mass_pre1[h]
-                                              : load_agent(a.stats + (head0 + h) * a.max_blocks + n);
-        score += mass * sm.f[h][s] * sm.invL[h];
-      }
-      const uint32_t key = score > 0.f ? __float_as_uint(score) : 0u;
-      sm.keys[n] = key;
-      kor |= key;
-      kand &= key;
-    }
-    if (n < kThreads) {
-      score0 = score;
-    } else if (a.score_out != nullptr) {
-      a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + n] = score;
-    }
-  }
-  if (a.idx_out != nullptr) topk_publish(sm, kor, kand);
-  __syncthreads();
-  if (a.idx_out != nullptr)
-    select_topk_block(sm, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k);
-  if (a.score_out != nullptr && (int)threadIdx.x < a.max_blocks)
-    a.score_out[((int64_t)b * a.num_kv_heads + g) * a.max_blocks + threadIdx.x] = score0;
-  store_outputs();
 }
 
-// Picks the epilogue instance whose load counts fit (b, g): kBatch split
-// partials per thread in a batch (more run in further batches), GP >= G.
-// Four instances: group <= 4 with up to 4 partials per thread, or more;
-// group <= 8; group <= 16.  Fewer instances than every (kBatch, GP) pair
-// measured faster on every shape tried (about 2% at 32K): the kernel's code
-// and register allocation shrink, and the extra filler loads of a loose fit
-// cost less.  Only the bf16 kernel with d = 128 (the large shapes) gets the
-// specialised instances; the others use one generic instance.
-template <int D, bool kSpecialise, bool kTwoLevel = false>
+// Epilogue of the scored mode.  After the per-head statistics, wavefronts
+// [0, kScoreWaves) turn the block masses into block scores (mass stored
+// relative to its split's max; f brings it to the head's max) and wavefront
+// 0 selects the top-k, while the other wavefronts merge the output; the two
+// groups meet at one barrier only, before the selection.  The masses of the
+// first MJ blocks of each score thread and kBatch output partials per merge
+// thread are loaded before the statistics are reduced.
+template <int D, int GP, int kBatch, bool kTwoLevel>
+__device__ __forceinline__ void epilogue_scored(const AttnArgs &a, int b, int g, int T, int nact,
+                                                EpiSmem &sm) {
+  constexpr int MJ = GP > 8 ? 2 : 4;
+  constexpr int HH = GP > kWaves ? 2 : 1;
+  const int G = a.group;
+  const int w = uniform(threadIdx.x >> 6);
+  const bool scorer = w < kScoreWaves;
+  const int64_t head0 = (int64_t)b * a.num_q_heads + g * G;
+  const int N = (T + kBlockTokens - 1) / kBlockTokens;
+  const int blocks_per_split = a.chunks_per_wg / kChunksPerBlock;
+  OutputMerge<D, kBatch, kTwoLevel> mg;
+  mg.init(a, head0, nact, scorer ? 0 : w - kScoreWaves, kWaves - kScoreWaves);
+  HeadStats<HH, kTwoLevel> hs;
+  hs.load_first(a, head0, nact, mg.nparts);
+  mg.issue_first(!scorer);
+  const __amdgpu_buffer_rsrc_t pst = buffer(a.stats + head0 * a.max_blocks,
+                                            (uint32_t)(G * a.max_blocks * 4));
+  float mass[MJ][GP];
+#pragma unroll
+  for (int j = 0; j < MJ; ++j)
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const int n = threadIdx.x + kScoreThreads * j;
+      const uint32_t off = (scorer && h < G && n < N)
+                               ? (uint32_t)((h * a.max_blocks + n) * 4)
+                               : 0x80000000u;
+      mass[j][h] =
+          __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pst, off, 0, kCoherent));
+    }
+  hs.load_rest(a, head0, nact);
+  hs.reduce(a, nact, mg.nparts, sm);
+  __syncthreads();
+
+  if (scorer) {
+    float *so = a.score_out != nullptr
+                    ? a.score_out + ((int64_t)b * a.num_kv_heads + g) * a.max_blocks
+                    : nullptr;
+    auto score_of = [&](int n, const float (&ms)[GP]) {
+      const int s = n / blocks_per_split;
+      float score = 0.f;
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+        if (h < G) score += ms[h] * sm.f[h][s] * sm.invL[h];
+      return score;
+    };
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+      const int n = threadIdx.x + kScoreThreads * j;
+      if (n < N) {
+        const float score = score_of(n, mass[j]);
+        sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
+        if (so != nullptr) so[n] = score;
+      } else if (so != nullptr && n < a.max_blocks) {
+        so[n] = 0.f;
+      }
+    }
+    for (int n = threadIdx.x + kScoreThreads * MJ; n < a.max_blocks; n += kScoreThreads) {
+      if (n < N) {
+        float ms[GP];
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+          ms[h] = h < G ? load_agent(a.stats + (head0 + h) * a.max_blocks + n) : 0.f;
+        const float score = score_of(n, ms);
+        sm.keys[n] = score > 0.f ? __float_as_uint(score) : 0u;
+        if (so != nullptr) so[n] = score;
+      } else if (so != nullptr) {
+        so[n] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // the score wavefronts return here: wavefront 0 selects (in epilogue())
+  if (!scorer) mg.run(a, head0, sm);
+}
+
+// Picks the epilogue instance whose load counts fit (b, g).  Scored mode:
+// group bound GP >= G (mass loads of GP heads) and the output partials each
+// merge thread loads at once.  Other modes: kBatch split partials per output
+// thread in a batch (more run in further batches) and heads per wavefront.
+// Only the bf16 kernel with d = 128 (the large shapes) gets specialised
+// instances; the others use one generic instance.
+template <int D, int kMode, bool kTwoLevel, bool kSpecialise>
 __device__ __forceinline__ void epilogue(const AttnArgs &a, int b, int g, int T, int nact, EpiSmem &sm) {
-  if constexpr (kTwoLevel) {
-    epilogue_impl<D, 8, kMaxGroup, true>(a, b, g, T, nact, sm);
-  } else if constexpr (!kSpecialise) {
-    epilogue_impl<D, 8, kMaxGroup>(a, b, g, T, nact, sm);
-  } else {
-    const int G = uniform(a.group);
-    const int stripes = kThreads / (G * (D / 4));
-    const int per = uniform((nact + stripes - 1) / stripes);
-    if (G <= 4) {
-      if (per <= 4)
-        epilogue_impl<D, 4, 4>(a, b, g, T, nact, sm);
-      else
-        epilogue_impl<D, 8, 4>(a, b, g, T, nact, sm);
-    } else if (G <= 8) {
-      epilogue_impl<D, 8, 8>(a, b, g, T, nact, sm);
+  if constexpr (kMode == kModeScored) {
+    if constexpr (!kSpecialise) {
+      epilogue_scored<D, kMaxGroup, 8, kTwoLevel>(a, b, g, T, nact, sm);
     } else {
-      epilogue_impl<D, 8, 16>(a, b, g, T, nact, sm);
+      const int G = uniform(a.group);
+      if (G <= 4)
+        epilogue_scored<D, 4, 16, kTwoLevel>(a, b, g, T, nact, sm);
+      else if (G <= 8)
+        epilogue_scored<D, 8, 16, kTwoLevel>(a, b, g, T, nact, sm);
+      else
+        epilogue_scored<D, 16, 8, kTwoLevel>(a, b, g, T, nact, sm);
+    }
+    // one copy of the selection for every instance above (keys in LDS)
+    if (uniform(threadIdx.x >> 6) == 0 && a.idx_out != nullptr) {
+      const int N = (T + kBlockTokens - 1) / kBlockTokens;
+      wave_select_topk(sm.keys, N, a.k, a.idx_out + ((int64_t)b * a.num_kv_heads + g) * a.k,
+                       sm.sel);
+    }
+  } else if constexpr (!kSpecialise || kTwoLevel) {
+    epilogue_plain<D, 8, 2, kTwoLevel, kMode>(a, b, g, nact, sm);
+  } else {
+    // partials per output thread: 8 wavefronts serve G * D / 4 items
+    const int G = uniform(a.group);
+    const int per_wave = (G * (D / 4) + kWaves - 1) / kWaves;
+    const int stripes = per_wave > 32 ? 1 : per_wave > 16 ? 2 : 4;
+    const int per = uniform((nact + stripes - 1) / stripes);
+    if (G <= 8) {
+      if (per <= 4)
+        epilogue_plain<D, 4, 1, false, kMode>(a, b, g, nact, sm);
+      else if (per <= 8)
+        epilogue_plain<D, 8, 1, false, kMode>(a, b, g, nact, sm);
+      else
+        epilogue_plain<D, 16, 1, false, kMode>(a, b, g, nact, sm);
+    } else {
+      epilogue_plain<D, 8, 2, false, kMode>(a, b, g, nact, sm);
     }
   }
 }
@@ -809,11 +1087,13 @@ __device__ __forceinline__ void epilogue(const AttnArgs &a, int b, int g, int T,
 struct Range {
   int T, C, c_begin, c_end, nact;
 };
-__device__ __forceinline__ bool wg_range(const AttnArgs &a, int s, int g, int b, int D, Range &r) {
-  r.T = clamp_ctx(scalar_load(a.ctx, b), a.max_blocks);
-  r.C = chunk_positions(r.T, a.sel, a.k);
+template <int kMode>
+__device__ __forceinline__ bool wg_range(const AttnArgs &a, int s, int g, int b, int D, int ctx_b,
+                                         Range &r) {
+  r.T = clamp_ctx(ctx_b, a.max_blocks);
+  r.C = chunk_positions<kMode>(r.T, a.k);
   if (r.C == 0) {
-    if (s == 0) write_empty(a, b, g, D);
+    if (s == 0) write_empty<kMode>(a, b, g, D);
     return false;
   }
   r.c_begin = s * a.chunks_per_wg;
@@ -843,16 +1123,21 @@ struct BfTile {
   u32x4 v[D / 16];
 };
 
-template <int D, bool kStaged, bool kTwoLevel = false>
+template <int D, int kMode, bool kTwoLevel = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_split_bf16(
     AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   __shared__ KernelSmem<D> sm;
   __shared__ int last_flag;
   Range r;
-  if (!wg_range(a, s, g, b, D, r)) return;
+  // the context length and the first chunk's block id and page are loaded
+  // together (prefetch_first)
+  const int ctx_b = scalar_load(a.ctx, b);
+  const FirstChunk first =
+      prefetch_first<kMode>(a, b, g, chunk_of(s * a.chunks_per_wg, uniform(threadIdx.x >> 6), 0));
+  if (!wg_range<kMode>(a, s, g, b, D, ctx_b, r)) return;
   const int T = r.T, c_begin = r.c_begin, c_end = r.c_end;
-  const bool want_mass = a.stats != nullptr;
+  constexpr bool want_mass = kMode == kModeScored;
 
   const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int quad = lane >> 4, m16 = lane & 15;
@@ -887,9 +1172,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // the range or without a readable page gets an empty resource: the loads
   // return zeros without touching memory, so every path issues the same loads
   // and the register tiles never need copying.
-  auto issue = [&](BfTile<D> &t, int pos, bool live) -> int {
+  auto issue = [&](BfTile<D> &t, int pos, bool live, bool is_first = false) -> int {
     int page = 0, sub = 0, valid = 0;
-    const bool ok = live && pos < c_end && resolve_chunk<kStaged>(a, b, g, T, pos, page, sub, valid);
+    const bool ok = live && pos < c_end &&
+                    (is_first ? resolve_first<kMode>(a, T, pos, first, page, sub, valid)
+                              : resolve_chunk<kMode>(a, b, g, T, pos, page, sub, valid));
     if (!ok) {
       page = 0;
       sub = 0;
@@ -990,7 +1277,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   BfTile<D> ta, tb;
   int i = 0;
   bool live = chunk_live(c_begin, c_end, w, 0);
-  int va = issue(ta, chunk_of(c_begin, w, 0), live);
+  int va = issue(ta, chunk_of(c_begin, w, 0), live, true);
   while (live) {
     const bool live_b = chunk_live(c_begin, c_end, w, i + 1);
     const int vb = issue(tb, chunk_of(c_begin, w, i + 1), live_b);
@@ -1013,8 +1300,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.split.o[w][4 * quad + r][16 * n + m16] = acc[n][r];
   __syncthreads();
-  if (!finish_split<D, kTwoLevel>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
-  epilogue<D, D == 128 && !kStaged, kTwoLevel>(a, b, g, T, r.nact, sm.epi);
+  if (!finish_split<D, kMode, kTwoLevel>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split,
+                                         &last_flag))
+    return;
+  epilogue<D, kMode, kTwoLevel, D == 128 && kMode != kModeStaged>(a, b, g, T, r.nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1022,16 +1311,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // the logits of token t over half of the head dimension for every head of the
 // group; p.V runs with lane i owning columns i and i+64.
 // ---------------------------------------------------------------------------
-template <int D, bool kStaged>
+template <int D, int kMode>
 __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   __shared__ KernelSmem<D> sm;
   __shared__ float q_s[kMaxGroup][D];
   __shared__ int last_flag;
   Range r;
-  if (!wg_range(a, s, g, b, D, r)) return;
+  if (!wg_range<kMode>(a, s, g, b, D, scalar_load(a.ctx, b), r)) return;
   const int T = r.T, c_begin = r.c_begin, c_end = r.c_end;
-  const bool want_mass = a.stats != nullptr;
+  constexpr bool want_mass = kMode == kModeScored;
 
   constexpr int CPL = D / 64;  // output columns per lane
   const int G = a.group;
@@ -1060,7 +1349,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) cmass[h] = 0.f;
     int page, sub, valid;
-    if (pos < c_end && resolve_chunk<kStaged>(a, b, g, T, pos, page, sub, valid)) {
+    if (pos < c_end && resolve_chunk<kMode>(a, b, g, T, pos, page, sub, valid)) {
       const int64_t tile = (int64_t)page * Hkv + g;
       const float *krow =
           kpool + (tile * kBlockTokens + sub * kChunkTokens + t) * D + half * (D / 2);
@@ -1139,32 +1428,30 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32(AttnArgs a) {
     for (int j = 0; j < CPL; ++j) sm.split.o[w][h][lane + 64 * j] = acc[h][j];
   }
   __syncthreads();
-  if (!finish_split<D>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag)) return;
-  epilogue<D, false>(a, b, g, T, r.nact, sm.epi);
+  if (!finish_split<D, kMode, false>(a, b, g, s, r.nact, c_begin, c_end, T, sm.split, &last_flag))
+    return;
+  epilogue<D, kMode, false, false>(a, b, g, T, r.nact, sm.epi);
 }
 
 // ---------------------------------------------------------------------------
-// Top-k of a caller-given score array: grid (Hkv, B).  Keys are the float bits
-// of the non-negative scores (monotone as unsigned integers).
+// Top-k of a caller-given score array: grid (Hkv, B).  Every thread loads
+// keys (the float bits of the non-negative scores, monotone as unsigned
+// integers) into LDS; wavefront 0 then selects.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void score_topk(TopkArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int T = clamp_ctx(a.ctx[b], a.max_blocks);
   const int N = (T + kBlockTokens - 1) / kBlockTokens;
-  __shared__ EpiSmem sm;
+  __shared__ uint32_t keys[kMaxBlocks];
+  __shared__ SelectSmem ss;
   const float *row = a.score + ((int64_t)b * a.num_kv_heads + g) * a.max_blocks;
-  topk_clear(sm);
-  uint32_t kor = 0u, kand = 0xFFFFFFFFu;
   for (int n = threadIdx.x; n < N; n += kThreads) {
     const float sc = row[n];
-    const uint32_t key = sc > 0.f ? __float_as_uint(sc) : 0u;
-    sm.keys[n] = key;
-    kor |= key;
-    kand &= key;
+    keys[n] = sc > 0.f ? __float_as_uint(sc) : 0u;
   }
-  topk_publish(sm, kor, kand);
   __syncthreads();
-  select_topk_block(sm, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k);
+  if (uniform(threadIdx.x >> 6) == 0)
+    wave_select_topk(keys, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k, ss);
 }
 
 // Kernel timers: while a timer runs, each launch of its kind takes an event
@@ -1239,27 +1526,45 @@ int timer_stop(int kind, double *total_ms, int *launches) {
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, int batch, void *stream) {
   const dim3 grid(a.nsplit, a.num_kv_heads, batch);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const TimerScope tm(a.sel != nullptr ? kTimerSparseAttn
-                      : a.stats != nullptr ? kTimerFullScored : kTimerFullAttn);
+  const int mode = a.sel != nullptr ? (a.staged ? kModeStaged : kModeSparse)
+                                    : (a.stats != nullptr ? kModeScored : kModeFull);
+  const TimerScope tm(mode_sparse(mode) ? kTimerSparseAttn
+                      : mode == kModeScored ? kTimerFullScored : kTimerFullAttn);
   const dim3 block(kThreads);
 #define HYLRA_LAUNCH(K) hipExtLaunchKernelGGL(K, grid, block, 0, st, tm.start, tm.stop, 0, a)
-  const bool staged = a.staged != 0;
-  if (dtype == 1) {
-    if (head_dim == 128) {
-      if (staged) HYLRA_LAUNCH((attn_split_bf16<128, true>));
-      else if (a.two_level) HYLRA_LAUNCH((attn_split_bf16<128, false, true>));
-      else HYLRA_LAUNCH((attn_split_bf16<128, false>));
-    } else {
-      if (staged) HYLRA_LAUNCH((attn_split_bf16<64, true>));
-      else HYLRA_LAUNCH((attn_split_bf16<64, false>));
+  if (dtype == 1 && head_dim == 128) {
+    switch (mode) {
+      case kModeFull:
+        if (a.two_level) HYLRA_LAUNCH((attn_split_bf16<128, kModeFull, true>));
+        else HYLRA_LAUNCH((attn_split_bf16<128, kModeFull, false>));
+        break;
+      case kModeScored:
+        if (a.two_level) HYLRA_LAUNCH((attn_split_bf16<128, kModeScored, true>));
+        else HYLRA_LAUNCH((attn_split_bf16<128, kModeScored, false>));
+        break;
+      case kModeSparse: HYLRA_LAUNCH((attn_split_bf16<128, kModeSparse>)); break;
+      default: HYLRA_LAUNCH((attn_split_bf16<128, kModeStaged>)); break;
+    }
+  } else if (dtype == 1) {
+    switch (mode) {
+      case kModeFull: HYLRA_LAUNCH((attn_split_bf16<64, kModeFull>)); break;
+      case kModeScored: HYLRA_LAUNCH((attn_split_bf16<64, kModeScored>)); break;
+      case kModeSparse: HYLRA_LAUNCH((attn_split_bf16<64, kModeSparse>)); break;
+      default: HYLRA_LAUNCH((attn_split_bf16<64, kModeStaged>)); break;
+    }
+  } else if (head_dim == 128) {
+    switch (mode) {
+      case kModeFull: HYLRA_LAUNCH((attn_split_f32<128, kModeFull>)); break;
+      case kModeScored: HYLRA_LAUNCH((attn_split_f32<128, kModeScored>)); break;
+      case kModeSparse: HYLRA_LAUNCH((attn_split_f32<128, kModeSparse>)); break;
+      default: HYLRA_LAUNCH((attn_split_f32<128, kModeStaged>)); break;
     }
   } else {
-    if (head_dim == 128) {
-      if (staged) HYLRA_LAUNCH((attn_split_f32<128, true>));
-      else HYLRA_LAUNCH((attn_split_f32<128, false>));
-    } else {
-      if (staged) HYLRA_LAUNCH((attn_split_f32<64, true>));
-      else HYLRA_LAUNCH((attn_split_f32<64, false>));
+    switch (mode) {
+      case kModeFull: HYLRA_LAUNCH((attn_split_f32<64, kModeFull>)); break;
+      case kModeScored: HYLRA_LAUNCH((attn_split_f32<64, kModeScored>)); break;
+      case kModeSparse: HYLRA_LAUNCH((attn_split_f32<64, kModeSparse>)); break;
+      default: HYLRA_LAUNCH((attn_split_f32<64, kModeStaged>)); break;
     }
   }
 #undef HYLRA_LAUNCH

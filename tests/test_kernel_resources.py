@@ -47,8 +47,9 @@ def resource_report(tmp_path, src=SRC):
 def test_attention_kernels_fit_without_scratch(tmp_path):
     kernels = resource_report(tmp_path)
     attn = {k: v for k, v in kernels.items() if "attn_split" in k}
-    # bf16 / f32, d 64 / 128, regular / staged pools, and the two-level merge of bf16 d 128
-    assert len(attn) == 9, sorted(kernels)
+    # bf16 / f32, d 64 / 128, four modes (full, scored, sparse, staged), and the
+    # two-level merge of bf16 d 128 in the two full modes
+    assert len(attn) == 18, sorted(kernels)
     for name, r in attn.items():
         assert r["ScratchSize"] == 0, (name, r)
         assert r["LDS"] <= 160 * 1024, (name, r)
