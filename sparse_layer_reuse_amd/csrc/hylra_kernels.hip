@@ -285,10 +285,11 @@ struct SplitSmem {
 };
 
 // LDS of the one-wavefront top-k selection.
-struct SelectSmem {
-  uint32_t cand_key[256];  // candidates of the filter, in ascending block id
+struct alignas(16) SelectSmem {
+  uint32_t cand_key[256 + 16];  // candidates of the filter, in ascending block id (+ zero pad)
   int32_t cand_id[256];
-  int hist[256];           // digit histogram of the radix fallback
+  int hist[256];                // digit histogram of the radix fallback
+  uint32_t lane_max[64];        // the filter's per-lane key maxima
 };
 
 // LDS used by the epilogue.
@@ -314,6 +315,46 @@ union KernelSmem {
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuad1032>(0u, v));
+  v = max(v, dpp_u32<kDppQuad2301>(0u, v));
+  v = max(v, dpp_u32<kDppRowHalfMirror>(0u, v));
+  v = max(v, dpp_u32<kDppRowMirror>(0u, v));
+  v = max(v, dpp_u32<kDppRowBcast15, 0xa>(0u, v));
+  v = max(v, dpp_u32<kDppRowBcast31, 0xc>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// For this lane's value v: how many of vals[0..n) are >= v (vals in LDS,
+// 16-byte aligned, n a wavefront-uniform multiple of 16).  Every read is one
+// address for the whole wavefront (a broadcast of four values), and the
+// comparisons feed four independent counters: plain vector ALU work with no
+// lane-to-scalar round trip per value.
+__device__ __forceinline__ int count_not_below(const uint32_t *vals, int n, uint32_t v) {
+  int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+  for (int j = 0; j < n; j += 16) {
+    u32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const u32x4 *>(&vals[j + 4 * u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      c0 += x[u][0] >= v ? 1 : 0;
+      c1 += x[u][1] >= v ? 1 : 0;
+      c2 += x[u][2] >= v ? 1 : 0;
+      c3 += x[u][3] >= v ? 1 : 0;
+    }
+  }
+  return c0 + c1 + c2 + c3;
+}
+
+// The kk-th largest (1 <= kk <= n) of values held one per lane, given each
+// lane's count c of values >= its own: the largest value with c >= kk (a
+// value above the kk-th largest has fewer than kk values at or above it).
+// Lanes with include == false take no part.
+__device__ __forceinline__ uint32_t kth_from_counts(uint32_t v, int c, int kk, bool include) {
+  return wave_max_u32(include && c >= kk ? v : 0u);
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -421,17 +462,12 @@ __device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&v)[NV], in
 }
 
 // Lower bound t0 of the k-th largest key (k <= 64).  Key n sits in lane
-// n % 64; the lanes are cut into R groups of S (R = 2k rounded up to a
-// power of two, at most 64), and t0 is the k-th largest of the R group
-// maxima: the largest key of at least k distinct groups, so at least k keys
-// are >= t0.  The k-th largest is found by counting, for each group maximum,
-// the maxima above it and those not below it (readlane broadcasts, every
-// comparison independent of the others).
-__device__ __forceinline__ uint32_t topk_filter(const uint32_t *keys, int N, int k) {
+// n % 64; t0 is the k-th largest of the 64 lane maxima.  At least k lanes
+// hold a key >= t0 (or t0 = 0 and every key is >= t0), so the k largest keys,
+// and every key equal to the k-th largest, are >= t0.
+__device__ __forceinline__ uint32_t topk_filter(const uint32_t *keys, int N, int k,
+                                                SelectSmem &ss) {
   const int lane = threadIdx.x & 63;
-  int R = 2;
-  while (R < 2 * k && R < 64) R <<= 1;
-  const int S = 64 / R;
   // this lane's largest key: four independent LDS reads per step
   uint32_t gm = 0u;
   for (int base = 0; base < N; base += 256) {
@@ -443,51 +479,29 @@ __device__ __forceinline__ uint32_t topk_filter(const uint32_t *keys, int N, int
     }
     gm = max(gm, max(max(v[0], v[1]), max(v[2], v[3])));
   }
-  if (S >= 2) gm = max(gm, dpp_u32<kDppQuad1032>(0u, gm));
-  if (S >= 4) gm = max(gm, dpp_u32<kDppQuad2301>(0u, gm));
-  if (S >= 8) gm = max(gm, dpp_u32<kDppRowHalfMirror>(0u, gm));
-  if (S >= 16) gm = max(gm, dpp_u32<kDppRowMirror>(0u, gm));
-  if (S >= 32) gm = max(gm, (uint32_t)__shfl_xor((int)gm, 16));
-  if (S >= 64) gm = max(gm, (uint32_t)__shfl_xor((int)gm, 32));
-  // every lane of a group holds its maximum; group r's sits at lane r * S.
-  // Four groups per step, each with its own counters (independent chains).
-  int above[4] = {0, 0, 0, 0}, not_below[4] = {0, 0, 0, 0};
-  for (int r0 = 0; r0 < R; r0 += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = r0 + u < R ? r0 + u : r0;  // R is a power of two >= 2
-      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)gm, r * S);
-      const bool in = r0 + u < R;
-      above[u] += (in && v > gm) ? 1 : 0;
-      not_below[u] += (in && v >= gm) ? 1 : 0;
-    }
-  }
-  const int ab = above[0] + above[1] + above[2] + above[3];
-  const int nb = not_below[0] + not_below[1] + not_below[2] + not_below[3];
-  const uint64_t hit = __ballot(ab < k && k <= nb);
-  return (uint32_t)__builtin_amdgcn_readlane((int)gm, __builtin_ctzll(hit));
+  ss.lane_max[lane] = gm;
+  wave_lds_sync();
+  return kth_from_counts(gm, count_not_below(ss.lane_max, 64, gm), k, true);
 }
 
 // Selection among C <= 64 candidates, candidate p in lane p, in ascending
-// block id: a candidate's rank is the number of candidates with a larger
-// key or an equal key and a lower id (readlane broadcasts, independent
-// comparisons); the keff of rank < keff are written in id order.
+// block id (cand_key zero past C up to a multiple of 16): the keff-th
+// largest key thr from the counts of keys >= each candidate's, then every
+// key above thr and the first keys equal to it, in id order, written in id
+// order to out[0..keff).
 __device__ __forceinline__ void select_candidates_rank(const SelectSmem &ss, int C, int keff,
                                                        int32_t *out) {
   const int lane = threadIdx.x & 63;
-  const uint32_t ck = lane < C ? ss.cand_key[lane] : 0u;
-  const int32_t ci = lane < C ? ss.cand_id[lane] : -1;
-  // four candidates per step, each with its own counter (independent chains)
-  int rank[4] = {0, 0, 0, 0};
-  for (int m0 = 0; m0 < C; m0 += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int m = m0 + u;
-      const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)ck, m < C ? m : m0);
-      rank[u] += (m < C && (km > ck || (km == ck && m < lane))) ? 1 : 0;
-    }
-  }
-  const bool sel = lane < C && rank[0] + rank[1] + rank[2] + rank[3] < keff;
+  const bool valid = lane < C;
+  const uint32_t ck = valid ? ss.cand_key[lane] : 0u;
+  const int32_t ci = valid ? ss.cand_id[lane] : -1;
+  // zero padding only adds to the counts of zero keys, which cannot move the
+  // keff-th largest: it is zero itself if a zero key reaches count keff
+  const uint32_t thr =
+      kth_from_counts(ck, count_not_below(ss.cand_key, (C + 15) & ~15, ck), keff, valid);
+  const int ngt = __builtin_popcountll(__ballot(valid && ck > thr));
+  const uint64_t eqm = __ballot(valid && ck == thr);
+  const bool sel = valid && (ck > thr || (ck == thr && lanes_below(eqm) < keff - ngt));
   const uint64_t selm = __ballot(sel);
   if (sel) out[lanes_below(selm)] = ci;
 }
@@ -531,9 +545,9 @@ __device__ __forceinline__ void select_candidates(const SelectSmem &ss, int C, i
 // indices written in ascending order to out[0..k_eff) and -1 after, up to k.
 //
 // A filter bound t0 (topk_filter) leaves the keys >= t0 as candidates,
-// usually a few more than k; they are compacted in id order and ranked
-// against each other (up to 64 of them), or the exact k-th largest among
-// them is found by ballot bisection (up to kMaxCandidates).  More
+// usually a few more than k; they are compacted in id order and the k-th
+// largest among them is found from broadcast counts (up to 64 of them) or
+// by ballot bisection (up to kMaxCandidates).  More
 // candidates, or k > 64, fall back to the radix select.
 // Either way the result is the exact top k under the tie rule.
 constexpr int kMaxCandidates = 256;
@@ -547,7 +561,7 @@ __device__ __forceinline__ void wave_select_topk(const uint32_t *keys, int N, in
   }
   bool done = false;
   if (k <= 64) {
-    const uint32_t t0 = topk_filter(keys, N, k);
+    const uint32_t t0 = topk_filter(keys, N, k, ss);
     int C = 0;
     for (int base = 0; base < N; base += 256) {
       uint32_t key[4];
@@ -569,6 +583,7 @@ __device__ __forceinline__ void wave_select_topk(const uint32_t *keys, int N, in
         C += __builtin_popcountll(bm);
       }
     }
+    if (C <= 64 && lane < 16) ss.cand_key[C + lane] = 0u;  // pad to a multiple of 16
     if (C <= kMaxCandidates) {
       wave_lds_sync();
       if (C <= 64)
