@@ -473,15 +473,26 @@ __device__ __forceinline__ uint32_t topk_filter(const uint32_t *keys, int N, int
   for (int base = 0; base < N; base += 256) {
     uint32_t v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int n = base + 64 * u + lane;
-      v[u] = n < N ? keys[n] : 0u;
-    }
+    for (int u = 0; u < 4; ++u) v[u] = keys[base + 64 * u + lane];
     gm = max(gm, max(max(v[0], v[1]), max(v[2], v[3])));
   }
   ss.lane_max[lane] = gm;
   wave_lds_sync();
   return kth_from_counts(gm, count_not_below(ss.lane_max, 64, gm), k, true);
+}
+
+// The same bound from 256 groups: group (u, lane) holds the keys n with
+// n % 256 == 64 u + lane, and t0 is the k-th largest of the 256 group maxima
+// (ballot bisection).  Finer groups than the lanes leave far fewer
+// candidates when k or the keys per lane are large.
+__device__ __forceinline__ uint32_t topk_filter256(const uint32_t *keys, int N, int k) {
+  const int lane = threadIdx.x & 63;
+  uint32_t gm[4] = {0u, 0u, 0u, 0u};
+  for (int base = 0; base < N; base += 256) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) gm[u] = max(gm[u], keys[base + 64 * u + lane]);
+  }
+  return wave_kth_largest<4>(gm, k);
 }
 
 // Selection among C <= 64 candidates, candidate p in lane p, in ascending
@@ -543,8 +554,10 @@ __device__ __forceinline__ void select_candidates(const SelectSmem &ss, int C, i
 // Top-k selection run by one whole wavefront: the k_eff = min(k, N) largest
 // keys[0..N) (unsigned compare, equal keys going to the lower index), their
 // indices written in ascending order to out[0..k_eff) and -1 after, up to k.
+// keys[N..) must be zero up to the next multiple of 256.
 //
-// A filter bound t0 (topk_filter) leaves the keys >= t0 as candidates,
+// A filter bound t0 (topk_filter for small k or N, else topk_filter256)
+// leaves the keys >= t0 as candidates,
 // usually a few more than k; they are compacted in id order and the k-th
 // largest among them is found from broadcast counts (up to 64 of them) or
 // by ballot bisection (up to kMaxCandidates).  More
@@ -561,15 +574,13 @@ __device__ __forceinline__ void wave_select_topk(const uint32_t *keys, int N, in
   }
   bool done = false;
   if (k <= 64) {
-    const uint32_t t0 = topk_filter(keys, N, k, ss);
+    const uint32_t t0 = (k <= 16 || N <= 256) ? topk_filter(keys, N, k, ss)
+                                              : topk_filter256(keys, N, k);
     int C = 0;
     for (int base = 0; base < N; base += 256) {
       uint32_t key[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int n = base + 64 * u + lane;
-        key[u] = n < N ? keys[n] : 0u;
-      }
+      for (int u = 0; u < 4; ++u) key[u] = keys[base + 64 * u + lane];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int n = base + 64 * u + lane;
@@ -1044,6 +1055,8 @@ __device__ __forceinline__ void epilogue_scored(const AttnArgs &a, int b, int g,
         so[n] = 0.f;
       }
     }
+    // the selection reads whole rows of 256 keys: zero the keys past N
+    for (int n = N + threadIdx.x; n < ((N + 255) & ~255); n += kScoreThreads) sm.keys[n] = 0u;
   }
   __syncthreads();
   // the score wavefronts return here: wavefront 0 selects (in epilogue())
@@ -1464,6 +1477,7 @@ __global__ __launch_bounds__(kThreads) void score_topk(TopkArgs a) {
     const float sc = row[n];
     keys[n] = sc > 0.f ? __float_as_uint(sc) : 0u;
   }
+  for (int n = N + threadIdx.x; n < ((N + 255) & ~255); n += kThreads) keys[n] = 0u;
   __syncthreads();
   if (uniform(threadIdx.x >> 6) == 0)
     wave_select_topk(keys, N, a.k, a.idx + ((int64_t)b * a.num_kv_heads + g) * a.k, ss);
