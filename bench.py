@@ -92,11 +92,12 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": mib << 20, "copies": 4}), flush=True)
 
 
-def measured_traffic(workload):
-    """HBM bytes per full-attention launch from the committed rocprofv3 PMC
-    summary of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a copy
-    kernel of known size), or None when there is none or when the kernel
-    source has changed since the counters were taken."""
+def measured_traffic(workload, scored):
+    """HBM bytes per full-attention launch (with fused block scores and
+    top-k when `scored`) from the committed rocprofv3 PMC summary of this
+    workload (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel of known
+    size), or None when there is none or when the kernel source has changed
+    since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "attn_traffic_%s.json" % workload)
     src = os.path.join(ROOT, "sparse_layer_reuse_amd", "csrc", "hylra_kernels.hip")
@@ -109,7 +110,7 @@ def measured_traffic(workload):
         return None
     if rec.get("kernel_source_sha256") != digest or rec.get("workload") != workload:
         return None
-    return rec.get("full_layer_traffic_bytes")
+    return rec.get("scored_layer_traffic_bytes" if scored else "full_layer_traffic_bytes")
 
 
 def policy_for(wl, hylra, theta, L, jump=None, profiled_layers=None, k=None):
@@ -347,6 +348,19 @@ def oracle_layer_times(wl, layers, src, k):
     return t_reset, t_reuse
 
 
+def reuse_similarity(M, src):
+    """Fidelity of a policy on the similarity matrix the DP runs on (row =
+    target layer, column = source): the similarity of every reuse layer to
+    the reset layer whose index set it attends -- the quantity the DP keeps
+    above its threshold and a static Jump-N schedule does not look at."""
+    sims = [float(M[j][s_]) for j, s_ in enumerate(src) if s_ != j]
+    if not sims:
+        return {"reuse_similarity_min": None, "reuse_similarity_mean": None,
+                "reuse_layers_below_0.8": 0}
+    return {"reuse_similarity_min": min(sims), "reuse_similarity_mean": sum(sims) / len(sims),
+            "reuse_layers_below_0.8": sum(1 for x in sims if x <= 0.8)}
+
+
 def measure_policy(layers, src, k, steps, warmup, torch, hylra, full_bytes, sparse_bytes):
     """One policy on resident layers: graph-replayed steps/s and the average
     launch time of each kernel kind (events stamped by the launches) with its
@@ -425,6 +439,8 @@ def measure_configs(args, torch, hylra):
             r = measure_policy(layers, src, k, steps, warmup, torch, hylra, full_bytes,
                                sparse_bytes)
             r["hybrid_over_full"] = r["steps_per_s"] / entry["full_steps_per_s"]
+            if wl.policy == "dp":
+                r.update(reuse_similarity(synth.workload_similarity(wl), src))
             if args.cpu_seconds > 0:
                 if oracle_t is None or oracle_t[2] != k:
                     tr, tu = oracle_layer_times(wl, layers, src, k)
@@ -696,7 +712,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(wl.name),
+            "traffic": measured_traffic(wl.name, scored_us is not None),
             "bytes_per_launch": full_bytes,
             "avg_launch_us": full_us,
         },

@@ -289,7 +289,7 @@ struct alignas(16) SelectSmem {
   uint32_t cand_key[256 + 16];  // candidates of the filter, in ascending block id (+ zero pad)
   int32_t cand_id[256];
   int hist[256];                // digit histogram of the radix fallback
-  uint32_t lane_max[64];        // the filter's per-lane key maxima
+  uint32_t lane_max[128];       // the filter's group maxima
 };
 
 // LDS used by the epilogue.
@@ -327,34 +327,41 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// For this lane's value v: how many of vals[0..n) are >= v (vals in LDS,
-// 16-byte aligned, n a wavefront-uniform multiple of 16).  Every read is one
-// address for the whole wavefront (a broadcast of four values), and the
-// comparisons feed four independent counters: plain vector ALU work with no
-// lane-to-scalar round trip per value.
-__device__ __forceinline__ int count_not_below(const uint32_t *vals, int n, uint32_t v) {
-  int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+// For each of this lane's NV values v[i]: how many of vals[0..n) are >= v[i]
+// (vals in LDS, 16-byte aligned, n a wavefront-uniform multiple of 16).
+// Every read is one address for the whole wavefront (a broadcast of four
+// values), and the comparisons feed four independent counters: plain vector
+// ALU work with no lane-to-scalar round trip per value.
+//
+// With these counts the kk-th largest of the values held across the lanes is
+// the largest value whose count reaches kk: a value above the kk-th largest
+// has fewer than kk values at or above it.
+template <int NV>
+__device__ __forceinline__ void count_not_below_n(const uint32_t *vals, int n,
+                                                  const uint32_t (&v)[NV], int (&c)[NV]) {
+  constexpr int A = NV >= 4 ? 1 : 4 / NV;  // counters per value
+  int acc[NV][A];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < A; ++e) acc[i][e] = 0;
   for (int j = 0; j < n; j += 16) {
     u32x4 x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const u32x4 *>(&vals[j + 4 * u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      c0 += x[u][0] >= v ? 1 : 0;
-      c1 += x[u][1] >= v ? 1 : 0;
-      c2 += x[u][2] >= v ? 1 : 0;
-      c3 += x[u][3] >= v ? 1 : 0;
-    }
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i][e % A] += x[u][e] >= v[i] ? 1 : 0;
   }
-  return c0 + c1 + c2 + c3;
-}
-
-// The kk-th largest (1 <= kk <= n) of values held one per lane, given each
-// lane's count c of values >= its own: the largest value with c >= kk (a
-// value above the kk-th largest has fewer than kk values at or above it).
-// Lanes with include == false take no part.
-__device__ __forceinline__ uint32_t kth_from_counts(uint32_t v, int c, int kk, bool include) {
-  return wave_max_u32(include && c >= kk ? v : 0u);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    c[i] = 0;
+#pragma unroll
+    for (int e = 0; e < A; ++e) c[i] += acc[i][e];
+  }
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -462,23 +469,35 @@ __device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&v)[NV], in
 }
 
 // Lower bound t0 of the k-th largest key (k <= 64).  Key n sits in lane
-// n % 64; t0 is the k-th largest of the 64 lane maxima.  At least k lanes
-// hold a key >= t0 (or t0 = 0 and every key is >= t0), so the k largest keys,
-// and every key equal to the k-th largest, are >= t0.
+// n % 64; the keys of a lane form NG groups (n / 64 % NG), and t0 is the
+// k-th largest of the 64 NG group maxima, found from each maximum's count
+// of maxima at or above it (broadcast reads).  At least k groups hold a key
+// >= t0 (or t0 = 0 and every key is >= t0), so the k largest keys, and
+// every key equal to the k-th largest, are >= t0.
+template <int NG>
 __device__ __forceinline__ uint32_t topk_filter(const uint32_t *keys, int N, int k,
                                                 SelectSmem &ss) {
   const int lane = threadIdx.x & 63;
-  // this lane's largest key: four independent LDS reads per step
-  uint32_t gm = 0u;
+  // four independent LDS reads per step
+  uint32_t gm[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) gm[i] = 0u;
   for (int base = 0; base < N; base += 256) {
     uint32_t v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = keys[base + 64 * u + lane];
-    gm = max(gm, max(max(v[0], v[1]), max(v[2], v[3])));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) gm[u % NG] = max(gm[u % NG], v[u]);
   }
-  ss.lane_max[lane] = gm;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) ss.lane_max[64 * i + lane] = gm[i];
   wave_lds_sync();
-  return kth_from_counts(gm, count_not_below(ss.lane_max, 64, gm), k, true);
+  int c[NG];
+  count_not_below_n<NG>(ss.lane_max, 64 * NG, gm, c);
+  uint32_t best = 0u;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) best = max(best, c[i] >= k ? gm[i] : 0u);
+  return wave_max_u32(best);
 }
 
 // The same bound from 256 groups: group (u, lane) holds the keys n with
@@ -495,26 +514,46 @@ __device__ __forceinline__ uint32_t topk_filter256(const uint32_t *keys, int N, 
   return wave_kth_largest<4>(gm, k);
 }
 
-// Selection among C <= 64 candidates, candidate p in lane p, in ascending
-// block id (cand_key zero past C up to a multiple of 16): the keff-th
-// largest key thr from the counts of keys >= each candidate's, then every
-// key above thr and the first keys equal to it, in id order, written in id
-// order to out[0..keff).
+// Selection among C <= 64 * NV candidates, candidate p in lane p % 64 (slot
+// p / 64), in ascending block id (cand_key zero past C up to a multiple of
+// 16): the keff-th largest key thr from the counts of keys >= each
+// candidate's, then every key above thr and the first keys equal to it, in
+// id order, written in id order to out[0..keff).
+template <int NV>
 __device__ __forceinline__ void select_candidates_rank(const SelectSmem &ss, int C, int keff,
                                                        int32_t *out) {
   const int lane = threadIdx.x & 63;
-  const bool valid = lane < C;
-  const uint32_t ck = valid ? ss.cand_key[lane] : 0u;
-  const int32_t ci = valid ? ss.cand_id[lane] : -1;
+  uint32_t ck[NV];
+  int32_t ci[NV];
+  bool valid[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    valid[i] = lane + 64 * i < C;
+    ck[i] = valid[i] ? ss.cand_key[lane + 64 * i] : 0u;
+    ci[i] = valid[i] ? ss.cand_id[lane + 64 * i] : -1;
+  }
+  int c[NV];
+  count_not_below_n<NV>(ss.cand_key, (C + 15) & ~15, ck, c);
   // zero padding only adds to the counts of zero keys, which cannot move the
   // keff-th largest: it is zero itself if a zero key reaches count keff
-  const uint32_t thr =
-      kth_from_counts(ck, count_not_below(ss.cand_key, (C + 15) & ~15, ck), keff, valid);
-  const int ngt = __builtin_popcountll(__ballot(valid && ck > thr));
-  const uint64_t eqm = __ballot(valid && ck == thr);
-  const bool sel = valid && (ck > thr || (ck == thr && lanes_below(eqm) < keff - ngt));
-  const uint64_t selm = __ballot(sel);
-  if (sel) out[lanes_below(selm)] = ci;
+  uint32_t best = 0u;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) best = max(best, valid[i] && c[i] >= keff ? ck[i] : 0u);
+  const uint32_t thr = wave_max_u32(best);
+  int ngt = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) ngt += __builtin_popcountll(__ballot(valid[i] && ck[i] > thr));
+  int eq_before = 0, taken = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint64_t eqm = __ballot(valid[i] && ck[i] == thr);
+    const bool sel = valid[i] && (ck[i] > thr ||
+                                  (ck[i] == thr && eq_before + lanes_below(eqm) < keff - ngt));
+    const uint64_t selm = __ballot(sel);
+    if (sel) out[taken + lanes_below(selm)] = ci[i];
+    taken += __builtin_popcountll(selm);
+    eq_before += __builtin_popcountll(eqm);
+  }
 }
 
 // Selection among the C (<= 64 * NV) candidates in ss, slot p = candidate p
@@ -556,11 +595,11 @@ __device__ __forceinline__ void select_candidates(const SelectSmem &ss, int C, i
 // indices written in ascending order to out[0..k_eff) and -1 after, up to k.
 // keys[N..) must be zero up to the next multiple of 256.
 //
-// A filter bound t0 (topk_filter for small k or N, else topk_filter256)
-// leaves the keys >= t0 as candidates,
-// usually a few more than k; they are compacted in id order and the k-th
-// largest among them is found from broadcast counts (up to 64 of them) or
-// by ballot bisection (up to kMaxCandidates).  More
+// A filter bound t0 (topk_filter over 64 or 128 groups; topk_filter256 when that leaves more
+// than kMaxCandidates) leaves the keys >= t0 as candidates, usually a few
+// more than k; they are compacted in id order and the k-th largest among
+// them is found from broadcast counts (up to 128 of them) or by ballot
+// bisection (up to kMaxCandidates).  More
 // candidates, or k > 64, fall back to the radix select.
 // Either way the result is the exact top k under the tie rule.
 constexpr int kMaxCandidates = 256;
@@ -574,31 +613,37 @@ __device__ __forceinline__ void wave_select_topk(const uint32_t *keys, int N, in
   }
   bool done = false;
   if (k <= 64) {
-    const uint32_t t0 = (k <= 16 || N <= 256) ? topk_filter(keys, N, k, ss)
-                                              : topk_filter256(keys, N, k);
-    int C = 0;
-    for (int base = 0; base < N; base += 256) {
-      uint32_t key[4];
+    // keys >= t0 to ss in id order (the first kMaxCandidates); returns how many
+    auto compact = [&](uint32_t t0) {
+      int C = 0;
+      for (int base = 0; base < N; base += 256) {
+        uint32_t key[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) key[u] = keys[base + 64 * u + lane];
+        for (int u = 0; u < 4; ++u) key[u] = keys[base + 64 * u + lane];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int n = base + 64 * u + lane;
-        const bool cand = n < N && key[u] >= t0;
-        const uint64_t bm = __ballot(cand);
-        const int pos = C + lanes_below(bm);
-        if (cand && pos < kMaxCandidates) {
-          ss.cand_key[pos] = key[u];
-          ss.cand_id[pos] = n;
+        for (int u = 0; u < 4; ++u) {
+          const int n = base + 64 * u + lane;
+          const bool cand = n < N && key[u] >= t0;
+          const uint64_t bm = __ballot(cand);
+          const int pos = C + lanes_below(bm);
+          if (cand && pos < kMaxCandidates) {
+            ss.cand_key[pos] = key[u];
+            ss.cand_id[pos] = n;
+          }
+          C += __builtin_popcountll(bm);
         }
-        C += __builtin_popcountll(bm);
       }
-    }
-    if (C <= 64 && lane < 16) ss.cand_key[C + lane] = 0u;  // pad to a multiple of 16
+      return C;
+    };
+    int C = compact(k <= 32 ? topk_filter<1>(keys, N, k, ss) : topk_filter<2>(keys, N, k, ss));
+    if (C > kMaxCandidates && N > 256) C = compact(topk_filter256(keys, N, k));
+    if (C <= 128 && lane < 16) ss.cand_key[C + lane] = 0u;  // pad to a multiple of 16
     if (C <= kMaxCandidates) {
       wave_lds_sync();
       if (C <= 64)
-        select_candidates_rank(ss, C, keff, out);
+        select_candidates_rank<1>(ss, C, keff, out);
+      else if (C <= 128)
+        select_candidates_rank<2>(ss, C, keff, out);
       else
         select_candidates<kMaxCandidates / 64>(ss, C, keff, out);
       done = true;
