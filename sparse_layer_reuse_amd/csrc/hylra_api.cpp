@@ -299,24 +299,37 @@ int report_error(int status, const char *message) {
   return fail(status, "%s", message);
 }
 
-// Split plans: about 256 workgroups per launch (one 8-wavefront workgroup
-// resident per compute unit on a 256-CU part) and at most kMaxWgChunks chunks
-// per workgroup.  Full mode: a multiple of 8 chunks per workgroup (one per
-// wavefront, and whole 128-token blocks, so a block's mass never straddles
-// two workgroups), at most kMaxSplits workgroups per (sequence, KV head).
-// Sparse mode: a multiple of 4 chunks, so a small selection spreads over
-// more compute units with one busy wavefront per SIMD (two wavefronts on one
-// SIMD share its vector issue), but at most as many splits as the merge reads
-// with one batch of 8 partial loads per thread (8 * 512 / (G * d / 4)).
+// Split plans: whole waves of 256 workgroups (one 8-wavefront workgroup
+// resident per compute unit on a 256-CU part) -- the fewest waves whose
+// chunks per workgroup fit kMaxWgChunks -- with the same number of splits
+// for every (sequence, KV head) row, so rows * nsplit never exceeds the
+// waves' slots: a partly filled extra wave would run its few workgroups on a
+// few compute units after the others have finished.  Full mode: a multiple
+// of 8 chunks per workgroup (one per wavefront, and whole 128-token blocks,
+// so a block's mass never straddles two workgroups), at most kMaxSplits
+// workgroups per row.  Sparse mode: a multiple of 4 chunks, so a small
+// selection spreads over more compute units with one busy wavefront per
+// SIMD (two wavefronts on one SIMD share its vector issue), but at most as
+// many splits as the merge reads with one batch of 8 partial loads per
+// thread (8 * 512 / (G * d / 4)).
 static_assert(kWavesPerGroup % kChunksPerBlock == 0, "a workgroup unit must hold whole blocks");
 constexpr long kTargetWorkgroups = 256;
 
 static SplitPlan make_plan(long chunks_per_seq, long rows, long unit, long max_splits) {
-  long cpw = (rows * chunks_per_seq + kTargetWorkgroups - 1) / kTargetWorkgroups;
   const long min_cpw = (chunks_per_seq + max_splits - 1) / max_splits;
-  if (cpw < min_cpw) cpw = min_cpw;
-  cpw = (cpw + unit - 1) / unit * unit;
-  if (cpw > kMaxWgChunks) cpw = kMaxWgChunks;  // nsplit <= 4 * 8192 / 256 <= kMaxSplits
+  long cpw = 0;
+  for (long waves = 1;; ++waves) {
+    long splits = waves * kTargetWorkgroups / rows;
+    if (splits < 1) splits = 1;
+    if (splits > max_splits) splits = max_splits;
+    cpw = (chunks_per_seq + splits - 1) / splits;
+    if (cpw < min_cpw) cpw = min_cpw;
+    cpw = (cpw + unit - 1) / unit * unit;
+    if (cpw <= kMaxWgChunks || splits == max_splits) break;
+  }
+  // a sparse merge bound below kMaxSplits can leave more chunks per split
+  // than kMaxWgChunks: then the splits grow past it (nsplit <= 4 * 8192 / 256)
+  if (cpw > kMaxWgChunks) cpw = kMaxWgChunks;
   SplitPlan p;
   p.chunks_per_wg = (int)cpw;
   p.nsplit = (int)((chunks_per_seq + cpw - 1) / cpw);
