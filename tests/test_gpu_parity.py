@@ -11,6 +11,8 @@ index set fed to the oracle.
 """
 import math
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -149,6 +151,77 @@ def test_block_topk_parity(H, case):
     else:
         s = rng.random((B, Hkv, mb)).astype(np.float32)
     ctx_np = np.array(ctx, np.int32)
+    idx = H.block_topk(torch.from_numpy(s).cuda(), torch.from_numpy(ctx_np).cuda(), k)
+    torch.cuda.synchronize()
+    want, _ = oracle.topk(s.astype(np.float64), ctx_np, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+
+
+def _lane_structured(rng, N, spread=0.8, noise=1e-4):
+    """Scores that depend mostly on the block id modulo 64 (the lane that
+    holds the key in a one-wavefront selection), so the blocks of the best
+    lanes are all near the top: a lane-maxima bound leaves many candidates."""
+    lane_val = rng.permutation(64) / 64.0
+    n = np.arange(N)
+    return (0.1 + spread * lane_val[n % 64] + noise * rng.random(N)).astype(np.float32)
+
+
+def _standouts_in_hot_lanes(rng, N):
+    """16 lanes whose keys all sit high (so a lane-maxima bound keeps them
+    all), each of their 64 (lane, n / 64 mod 4) classes holding one standout
+    key (so the 256-group bound singles the standouts out)."""
+    n = np.arange(N)
+    lane, u = n % 64, (n // 64) % 4
+    top = rng.choice(64, 16, replace=False)
+    s = 0.1 + 0.2 * rng.random(N)
+    hot = np.isin(lane, top)
+    s[hot] = 0.6 + 0.01 * rng.random(int(hot.sum()))
+    for l in top:
+        for uu in range(4):
+            s[rng.choice(np.nonzero((lane == l) & (u == uu))[0])] = 0.9 + 0.05 * rng.random()
+    return s.astype(np.float32)
+
+
+# Score rows built to send the one-wavefront selection down each of its
+# paths (comments give the candidate count after the filter bound).
+SELECTION_PATH_CASES = {
+    # 150 blocks share the top score: 150 candidates, ballot bisection; the
+    # 40 lowest ids among them win
+    # lane-structured, 8 keys per lane: ~250 distinct candidates, bisection
+    "bisection_distinct": (512, 32, lambda rng, N: _lane_structured(rng, N)),
+    # 8 levels, ~32 blocks at the top one: ranked by counts with a tie at the cut
+    "rank1_ties": (256, 16, lambda rng, N: (rng.integers(1, 9, N) / 8.0).astype(np.float32)),
+    "bisection_ties": (256, 40, lambda rng, N: np.where(
+        np.isin(np.arange(N), rng.choice(N, 150, replace=False)), 0.75,
+        0.1 + 0.4 * rng.random(N)).astype(np.float32)),
+    # the 32 best lanes hold all their 16 keys above the lane bound (~500
+    # candidates): the 256-group bound is computed and the keys compacted
+    # again (~120 candidates, two per lane); with k 64, 64 standouts
+    "refilter_k32": (1024, 32, lambda rng, N: _lane_structured(rng, N)),
+    "refilter_k64": (4096, 64, _standouts_in_hot_lanes),
+    # 128 lane-structured groups at k 64 (candidates ~64-128): two per lane
+    "rank2_k64": (1024, 64, lambda rng, N: rng.random(N).astype(np.float32)),
+    # every score equal: more than 256 candidates after both bounds, radix
+    # select, ids 0..k-1
+    "radix_all_equal": (2048, 64, lambda rng, N: np.full(N, 0.5, np.float32)),
+    # three levels, ~1000 blocks at the top one: radix after both bounds
+    "radix_three_levels": (3000, 48, lambda rng, N: (rng.integers(1, 4, N) / 4.0).astype(np.float32)),
+    # zero scores among the top k (keys of zero are valid candidates): ranked
+    # by counts (100 candidates), and through the radix select (300)
+    "zeros_rank2": (100, 20, lambda rng, N: np.where(np.arange(N) < 10, 0.9,
+                                                      0.0).astype(np.float32)),
+    "zeros_radix": (300, 20, lambda rng, N: np.where(np.arange(N) < 10, 0.9,
+                                                      0.0).astype(np.float32)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SELECTION_PATH_CASES))
+def test_block_topk_selection_paths(H, name):
+    N, k, make = SELECTION_PATH_CASES[name]
+    say("block_topk path", name, "N", N, "k", k)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    s = np.stack([make(rng, N) for _ in range(2)])[None]  # [B=1][Hkv=2][N]
+    ctx_np = np.array([N * 128], np.int32)
     idx = H.block_topk(torch.from_numpy(s).cuda(), torch.from_numpy(ctx_np).cuda(), k)
     torch.cuda.synchronize()
     want, _ = oracle.topk(s.astype(np.float64), ctx_np, k)
