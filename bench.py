@@ -223,6 +223,38 @@ def stream_ceiling(torch, hylra, mib=512, buffers=4, reps=3):
             "launches": launches, "kernel": "read_probe (hylra_read_probe)"}
 
 
+def settle(torch, hylra, max_s=30.0):
+    """Waits until nothing else takes HBM bandwidth: device memory released
+    by an earlier process (or an earlier workload of this run) is cleared by
+    the driver in the background for several seconds, and a run started
+    meanwhile streams ~5% slower.  Reads a 512 MiB buffer with the read
+    probe until its rate reaches 97% of a 7.0 TB/s idle ceiling, or stops
+    rising for 5 s after at least 10 s, or max_s pass.  Returns the seconds
+    waited and the last rate (GB/s)."""
+    buf = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    best, best_t, rate = 0.0, t0, 0.0
+    while True:
+        start.record()
+        for _ in range(8):
+            hylra.read_probe(buf, sink)
+        stop.record()
+        torch.cuda.synchronize()
+        rate = 8 * (512 << 20) / (start.elapsed_time(stop) * 1e-3) / 1e9
+        now = time.time()
+        if rate > best * 1.01:
+            best, best_t = rate, now
+        if rate >= 0.97 * 7000.0 or now - t0 >= max_s or \
+                (now - t0 >= 10.0 and now - best_t >= 5.0):
+            break
+        time.sleep(0.25)
+    del buf
+    return time.time() - t0, rate
+
+
 def cpu_baseline(wl, layers, src, k, budget_s):
     """Oracle timed on the host: passes over the step's layers in order (the
     carried indices flow from each reset layer to its reuse layers) until the
@@ -395,10 +427,10 @@ def measure_configs(args, torch, hylra):
     (labelled extrapolated)."""
     from sparse_layer_reuse_amd import synth, workloads as W
     plans = [
-        ("llama3_8b_b8_64k_dp", [("dp", 0.8, 32), ("jump", 3, 32), ("jump", 4, 32)]),
-        ("llama3_8b_paged_128k", [("fixed", None, 8), ("fixed", None, 32), ("fixed", None, 64)]),
         ("llama3_70b_128k_dp", [("dp", 0.7, 32), ("dp", 0.8, 32), ("dp", 0.9, 32),
                                 ("jump", 3, 32), ("jump", 4, 32)]),
+        ("llama3_8b_b8_64k_dp", [("dp", 0.8, 32), ("jump", 3, 32), ("jump", 4, 32)]),
+        ("llama3_8b_paged_128k", [("fixed", None, 8), ("fixed", None, 32), ("fixed", None, 64)]),
     ]
     steps, warmup = args.config_steps, 3
     out = {}
@@ -408,6 +440,7 @@ def measure_configs(args, torch, hylra):
         layers = synth.workload_layers(wl, device="cuda")
         torch.cuda.synchronize()
         gen_s = time.time() - t0
+        settle_s, settle_gbs = settle(torch, hylra)
         full_bytes = wl.kv_bytes_per_layer()
         full = hylra.FullPlan(layers)
         _, kf = timed(full.run, steps, warmup, torch, (hylra.KERNEL_FULL_ATTN,), hylra)
@@ -418,6 +451,7 @@ def measure_configs(args, torch, hylra):
             "batch": wl.batch, "layers": wl.layers, "num_q_heads": wl.num_q_heads,
             "num_kv_heads": wl.num_kv_heads, "ctx": wl.ctx, "paged": wl.paged,
             "kv_bytes_per_layer": full_bytes, "input_generation_s": gen_s,
+            "settle": {"seconds": settle_s, "read_gbs": settle_gbs},
             "full_steps_per_s": 1000.0 / ms_full, "full_layer_us": full_us,
             "frac_full_layer": full_bytes / (full_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "policies": {},
@@ -636,6 +670,7 @@ def main():
 
     hybrid = hylra.PolicyPlan(layers, src, k)
     ALL = (hylra.KERNEL_FULL_SCORED, hylra.KERNEL_FULL_ATTN, hylra.KERNEL_SPARSE_ATTN)
+    settle_s, settle_gbs = settle(torch, hylra)
     # eager steps with per-kernel HIP events (per-layer latency, roofline)
     ms_eager, kern = timed(hybrid.run, args.steps, args.warmup, torch, ALL, hylra)
     # the step as one HIP graph (how a decode loop replays a static step): value
@@ -643,6 +678,7 @@ def main():
     p10, p50, p90 = step_percentiles(graph_h, args.steps, torch)
     del graph_h
     result_extra = {"eager_steps_per_s": 1000.0 / ms_eager, "eager_ms_per_step": ms_eager,
+                    "settle": {"seconds": settle_s, "read_gbs": settle_gbs},
                     "step_ms_p10_p50_p90": [p10, p50, p90]}
     if not args.skip_baselines:
         full = hylra.FullPlan(layers)
