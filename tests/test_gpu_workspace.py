@@ -142,3 +142,53 @@ def test_workspace_reused_across_shapes_matches_fresh(H):
                                          num_kv_heads=1)
     assert np.abs(got[6].cpu().numpy() - r_out).max() <= 2e-3
     assert np.abs(got[7].cpu().numpy() - r_lse).max() <= 2e-3
+
+
+def test_random_call_sequence_on_one_workspace(H):
+    """Twelve seeded calls of random shapes and entry points (full layers
+    with and without scores, sparse layers over random id rows with padding
+    and repeats, policy steps) on one shared workspace, each bit-identical to
+    the same call on a fresh workspace."""
+    rng = np.random.default_rng(2024)
+    calls = []
+    for i in range(12):
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 4, 8]))
+        B = int(rng.integers(1, 4))
+        ctx = tuple(int(t) for t in rng.integers(0, 9000, size=B))
+        k = int(rng.integers(1, 24))
+        kind = str(rng.choice(["full", "scored", "sparse", "policy"]))
+        lay = layer(dtype, ctx, G * Hkv, Hkv, d, seed=3000 + i)
+        calls.append((kind, lay, k, ctx))
+    size = max(int(fresh_ws(H, lay, k).numel()) for _, lay, k, _ in calls)
+    shared = torch.zeros(size, dtype=torch.uint8, device="cuda")
+
+    def run(kind, lay, k, ctx, ws, i):
+        args = (lay["q"], lay["k_pool"], lay["v_pool"], lay["table"], lay["ctx"])
+        if kind == "full":
+            out, lse, _ = H.decode_full(*args, ws=ws)
+            return [out, lse]
+        if kind == "scored":
+            out, lse, score = H.decode_full(*args, want_scores=True, ws=ws)
+            return [out, lse, score]
+        if kind == "sparse":
+            nb = lay["table"].shape[1]
+            g = torch.Generator().manual_seed(4000 + i)
+            idx = torch.randint(-1, nb + 2, (len(ctx), lay["k_pool"].shape[1], k),
+                                dtype=torch.int32, generator=g).cuda()
+            out, lse = H.decode_sparse(*args, idx, ws=ws)
+            return [out, lse]
+        layers = [lay, lay, lay]
+        outs, lses = H.PolicyPlan(layers, [0, 0, 2], k, ws=ws).run()
+        return [o.clone() for o in outs] + [l.clone() for l in lses]
+
+    for i, (kind, lay, k, ctx) in enumerate(calls):
+        say("call", i, kind, ctx, "k", k, str(lay["q"].dtype))
+        counters_zero(shared, "before call %d" % i)
+        got = [t.clone() for t in run(kind, lay, k, ctx, shared, i)]
+        want = run(kind, lay, k, ctx, fresh_ws(H, lay, k), i)
+        for j, (a, b) in enumerate(zip(got, want)):
+            same(a, b, "call %d (%s) result %d" % (i, kind, j))
+    counters_zero(shared, "after the sequence")
