@@ -496,12 +496,17 @@ PREFIX = 8
 
 @pytest.mark.parametrize("name,k,theta", [
     ("llama3_8b_b8_64k_dp", 32, None),
+    ("llama3_8b_paged_128k", 8, None),
     ("llama3_8b_paged_128k", 32, None),
+    ("llama3_8b_paged_128k", 64, None),
+    ("llama3_70b_128k_dp", 32, 0.7),
     ("llama3_70b_128k_dp", 32, 0.8),
+    ("llama3_70b_128k_dp", 32, 0.9),
 ])
 def test_run_policy_large_workload_all_layers(H, name, k, theta):
     """Every layer and every sequence of the 64K-128K workloads, at full
-    size in the benchmark's launch configuration, against the oracle."""
+    size in the benchmark's launch configuration and for each top-k and
+    threshold the benchmark runs them with, against the oracle."""
     wl = W.get(name)
     src = workload_src(H, wl, theta)
     say("run_policy all layers", name, "k", k, "theta", theta, "resets",
