@@ -559,6 +559,24 @@ def test_run_policy_large_workload_prefix(H, name, k, theta):
                     assert got <= want, "layer %d seq %d head %d" % (j, b, g)
 
 
+@pytest.mark.parametrize("name,jump", [
+    ("llama3_8b_b8_64k_dp", 3), ("llama3_8b_b8_64k_dp", 4),
+    ("llama3_70b_128k_dp", 3), ("llama3_70b_128k_dp", 4),
+])
+def test_run_policy_large_workload_jump_prefix(H, name, jump):
+    """The Jump-N policies the benchmark runs beside the DP policy (a reset
+    every N layers), at full per-layer size: the first eight layers, checked
+    for the first and the last sequence of the batch."""
+    wl = W.get(name)
+    src = W.src_from_resets(wl.layers, tuple(range(0, wl.layers, jump)))[:PREFIX]
+    say("run_policy jump", jump, name, "src", src)
+    layers = synth.workload_layers(wl, device="cuda", layers=range(PREFIX))
+    k = wl.topk[0]
+    n, *_ = check_policy_run(H, layers, src, k, wl.dtype, wl.num_kv_heads,
+                             seqs=sorted({0, wl.batch - 1}))
+    assert n == PREFIX
+
+
 # The bf16 d=128 merge is compiled in instances sized by the split partials
 # each merge thread reads (ceil(splits / stripes), stripes = 512 / (G * d / 4)
 # threads per split: up to 2, 4, 8 and more, in batches) and by the group size bound
